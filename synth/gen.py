@@ -1,0 +1,57 @@
+"""Seeded input generation.
+
+Recipe: numpy Generator(PCG64(seed)); draw, in this order,
+  1. the per-sequence valid lengths (only for padded workloads), integers
+     uniform in [len_lo, len_hi] inclusive;
+  2. Q, then K, then V as float32 standard normals of the full buffer shape,
+     each multiplied by the workload's amplitude;
+then cast to the storage dtype (bf16: round to nearest even, done by torch).
+The fp32 copies returned for the oracle hold exactly the values the GPU sees.
+Optionally the padded region (keys at or beyond the valid length, query rows
+beyond the live rows) is overwritten with NaN to prove outputs never read it.
+"""
+
+import numpy as np
+import torch
+
+
+def _draw(rng, shape, amp):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if amp != 1.0:
+        x *= np.float32(amp)
+    return x
+
+
+def make_inputs(w, seed, pad_fill="draw"):
+    """Returns a dict:
+        q, k, v        torch CPU tensors in the storage dtype, contiguous
+        q32, k32, v32  numpy float32 arrays with the same values
+        seqlens        numpy int32 [B] or None
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqlens = None
+    if w.padded:
+        seqlens = rng.integers(w.len_lo, w.len_hi, size=w.B,
+                               endpoint=True).astype(np.int32)
+    qs = (w.B, w.Hq, w.Nq, w.d)
+    ks = (w.B, w.Hkv, w.Nk, w.d)
+    arrs = [_draw(rng, qs, w.amp), _draw(rng, ks, w.amp),
+            _draw(rng, ks, w.amp)]
+    if pad_fill == "nan":
+        lens = seqlens if seqlens is not None else np.full(w.B, w.Nk)
+        for b in range(w.B):
+            vl = int(lens[b])
+            arrs[1][b, :, vl:] = np.nan
+            arrs[2][b, :, vl:] = np.nan
+            if w.Nq == w.Nk:
+                arrs[0][b, :, vl:] = np.nan
+    elif pad_fill != "draw":
+        raise ValueError(pad_fill)
+    out = {"seqlens": seqlens}
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    for name, a in zip(("q", "k", "v"), arrs):
+        t = torch.from_numpy(a).to(tdt).contiguous()
+        out[name] = t
+        out[name + "32"] = a if tdt == torch.float32 else \
+            t.to(torch.float32).numpy()
+    return out

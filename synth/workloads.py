@@ -1,0 +1,64 @@
+"""The five workload shapes: one fp32 correctness case, three bf16 prefill
+cases and one bf16 decode step.
+
+They stand in for the pages' workloads (GPT-2 / BERT / long-context models);
+no dataset or trained weight is used: Q, K and V are i.i.d. normal draws of
+the stated shape, and valid lengths are uniform draws (right padding).
+"""
+
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str            # "fp32" or "bf16"
+    causal: bool
+    window: int = 0       # 0 = no window
+    len_lo: int = 0       # valid lengths drawn uniformly from [len_lo, len_hi]
+    len_hi: int = 0       # (both 0: every sequence is full length)
+    amp: float = 1.0      # Q, K, V = amp * N(0, 1)
+
+    @property
+    def padded(self):
+        return self.len_hi > 0
+
+    @property
+    def scale(self):
+        return 1.0 / (self.d ** 0.5)
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+WORKLOADS = (
+    # single head, fp32, no mask: the small correctness case
+    Workload("fp32-single-head", B=1, Hq=1, Hkv=1, Nq=128, Nk=128, d=64,
+             dtype="fp32", causal=False),
+    # GPT-2-small-shaped causal MHA with right padding
+    Workload("gpt2-small-causal-padded", B=16, Hq=12, Hkv=12, Nq=1024,
+             Nk=1024, d=64, dtype="bf16", causal=True, len_lo=512,
+             len_hi=1024),
+    # grouped-query causal prefill, 7 query heads per K/V head
+    Workload("gqa-causal-prefill", B=4, Hq=28, Hkv=4, Nq=4096, Nk=4096,
+             d=128, dtype="bf16", causal=True, amp=0.5),
+    # sliding-window causal attention: self plus the previous 1023 keys
+    Workload("sliding-window-causal", B=2, Hq=16, Hkv=16, Nq=16384,
+             Nk=16384, d=64, dtype="bf16", causal=True, window=1024),
+    # one decode step against a padded KV cache
+    Workload("decode-gqa", B=64, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128,
+             dtype="bf16", causal=True, len_lo=2048, len_hi=8192),
+)
+
+
+def by_name(name):
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
