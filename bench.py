@@ -1,0 +1,301 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path on resident synthetic inputs:
+  1. bf16 causal GQA prefill  B=4 Hq=28 Hkv=4 N=4096 d=128 (the headline),
+  2. bf16 decode step         B=64 Hq=32 Hkv=8 d=128, cache lengths U[2048,8192],
+  3. fp32 single-head case    B=1 H=1 N=128 d=64.
+`value` is the prefill throughput in algorithmic TFLOP/s (4*d FLOPs per
+allowed query/key pair, both matrix products, masked pairs not counted); the
+decode step is reported in algorithmic HBM GB/s (valid K/V bytes + q + o +
+lse).  Per-launch durations come from HIP events recorded on the stream the
+kernels run on.  The fp64 CPU oracle is timed on a bounded sample of the
+prefill workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
+                       [--no-cpu-baseline]
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention fwd TFLOP/s (bf16 causal prefill) + decode HBM GB/s, "
+          "% of roofline")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "prefill": "transformer_self_attention_attn_amd/csrc/prefill_bf16.hip",
+    "decode": "transformer_self_attention_attn_amd/csrc/decode_bf16.hip",
+}
+
+
+def allowed_pairs(w, seqlens):
+    """Number of allowed (query, key) pairs per head, summed over batch."""
+    import numpy as np
+    total = 0
+    for b in range(w.B):
+        L = w.Nk if seqlens is None else int(min(max(seqlens[b], 0), w.Nk))
+        live = L if w.Nq == w.Nk else w.Nq
+        i = np.arange(live, dtype=np.int64)
+        pos = i + (L - live)
+        hi = np.minimum(L, pos + 1) if w.causal else np.full_like(i, L)
+        lo = np.maximum(0, pos - w.window + 1) if w.window > 0 else \
+            np.zeros_like(i)
+        total += int(np.maximum(hi - lo, 0).sum())
+    return total
+
+
+def decode_bytes(w, seqlens):
+    keys = allowed_pairs(w, seqlens)  # one query row per (b, h): keys per b
+    kv = keys * w.Hkv * w.d * 2 * 2
+    q = w.B * w.Hq * w.d * 2
+    o = w.B * w.Hq * w.d * 2
+    lse = w.B * w.Hq * 4
+    return kv + q + o + lse
+
+
+def trimmed(ms):
+    """SpAtten review, EVALUATION - latency protocol: drop the largest and
+    the smallest 15% of the repetitions, average the middle 70%."""
+    s = sorted(ms)
+    n = len(s)
+    cut = int(round(0.15 * n))
+    mid = s[cut:n - cut] or s
+    return dict(trimmed_mean_ms=sum(mid) / len(mid), p50_ms=s[n // 2],
+                min_ms=s[0], reps=n)
+
+
+def source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kind):
+    """HBM bytes per launch from committed rocprofv3 counter runs, only if
+    they were taken on the kernel source as it is now."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kind)
+    if not rec or rec.get("source_sha256") != source_sha(KERNEL_SOURCES[kind]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s=20.0):
+    """Times the fp64 oracle (as it stands) on whole heads of batch 0 of the
+    prefill workload until about `budget_s` seconds of CPU work are done."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()]
+                      or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    q32, k32, v32 = x["q32"], x["k32"], x["v32"]
+    heads_done = 0
+    t_total = 0.0
+    per_head_pairs = allowed_pairs(w.with_(B=1), None)
+    g = w.Hq // w.Hkv
+    while t_total < budget_s and heads_done < w.Hq:
+        h = heads_done
+        hk = h // g
+        t0 = time.perf_counter()
+        oracle.attention(q32[:1, h:h + 1], k32[:1, hk:hk + 1],
+                         v32[:1, hk:hk + 1], scale=w.scale, causal=w.causal,
+                         window=w.window, seqlens=None)
+        t_total += time.perf_counter() - t0
+        heads_done += 1
+    flops = 4.0 * w.d * per_head_pairs * heads_done
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"{heads_done} of {w.B * w.Hq} (batch, head) slices "
+                       f"of {w.name} (batch 0, all {w.Nq} query rows each), "
+                       f"{t_total:.1f} s, fp64 NumPy"),
+            "seconds": t_total}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=200,
+                    help="repetitions of the trimmed-mean latency protocol")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus "
+              f"{args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import transformer_self_attention_attn_amd as mi
+    mi.load()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = synth.by_name("gqa-causal-prefill")
+    wd = synth.by_name("decode-gqa")
+    wf = synth.by_name("fp32-single-head")
+    xp = synth.make_inputs(wp, 3)
+    xd = synth.make_inputs(wd, 5)
+    xf = synth.make_inputs(wf, 1)
+
+    def dev_in(x):
+        sl = None
+        if x["seqlens"] is not None:
+            sl = torch.from_numpy(x["seqlens"]).to(dev)
+        return [x["q"].to(dev), x["k"].to(dev), x["v"].to(dev), sl]
+
+    P = dev_in(xp)
+    D0 = dev_in(xd)
+    # a second copy of the decode cache: consecutive steps alternate between
+    # them so a decode step never finds the previous step's K/V in cache
+    D1 = [D0[0], D0[1].clone(), D0[2].clone(), D0[3]]
+    F = dev_in(xf)
+    po = torch.empty_like(P[0])
+    pl = torch.empty(P[0].shape[:3], dtype=torch.float32, device=dev)
+    do = torch.empty_like(D0[0])
+    dl = torch.empty(D0[0].shape[:3], dtype=torch.float32, device=dev)
+    fo = torch.empty_like(F[0])
+    fl = torch.empty(F[0].shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        mi.attn(P[0], P[1], P[2], causal=True, seqlens=P[3], out=po, lse=pl)
+
+    def decode(i):
+        Dx = D0 if i % 2 == 0 else D1
+        mi.attn(Dx[0], Dx[1], Dx[2], causal=True, seqlens=Dx[3], out=do,
+                lse=dl)
+
+    def fp32():
+        mi.attn(F[0], F[1], F[2], causal=False, seqlens=F[3], out=fo,
+                lse=fl)
+
+    for i in range(args.warmup):
+        prefill()
+        decode(i)
+        fp32()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        decode(i)
+        e[2].record(stream)
+        fp32()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    f32_ms = [e[2].elapsed_time(e[3]) for e in ev]
+
+    flops = 4.0 * wp.d * allowed_pairs(wp, xp["seqlens"]) * wp.Hq
+    dbytes = float(decode_bytes(wd, xd["seqlens"]))
+    pre_avg = sum(pre_ms) / K
+    dec_avg = sum(dec_ms) / K
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    gbs = dbytes / (dec_avg * 1e-3) / 1e9
+
+    # latency protocol: R single-kernel repetitions each, trimmed mean
+    def reps(fn):
+        out = []
+        for i in range(args.reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+            out.append((a, b))
+        torch.cuda.synchronize()
+        return trimmed([a.elapsed_time(b) for a, b in out])
+
+    proto_p = reps(lambda i: prefill())
+    proto_d = reps(decode)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws; no dataset or weights)",
+        "config": {
+            "workload": ("gqa-causal-prefill: B=4 Hq=28 Hkv=4 N=4096 d=128 "
+                         "bf16 causal, Q/K/V = 0.5*N(0,1), seed 3; the step "
+                         "also runs decode-gqa (B=64 Hq=32 Hkv=8 d=128 bf16, "
+                         "cache lengths U[2048,8192], seed 5) and "
+                         "fp32-single-head (B=1 H=1 N=128 d=64)"),
+            "global_batch": wp.B,
+            "seq_len": wp.Nq,
+            "parallelism": "none (one GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for("prefill"),
+            "kernel": "prefill_kernel<128>",
+            "algorithmic_flop_per_launch": flops,
+            "avg_launch_ms": round(pre_avg, 5),
+        },
+        "decode": {
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for("decode"),
+                "kernels": "decode_split_kernel<128,4> + "
+                           "decode_combine_kernel<128>",
+                "algorithmic_bytes_per_launch": dbytes,
+                "avg_launch_ms": round(dec_avg, 5),
+            },
+        },
+        "fp32_case_avg_ms": round(sum(f32_ms) / K, 5),
+        "latency_protocol": {"prefill": proto_p, "decode": proto_d},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wp, xp)
+        line["cpu_baseline"]["gpu_over_cpu"] = round(
+            tflops / line["cpu_baseline"]["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

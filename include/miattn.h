@@ -1,0 +1,100 @@
+/*
+ * libmiattn: forward multi-head scaled dot-product attention on gfx950.
+ *
+ *   O = softmax(scale * Q K^T + mask) V,    lse = log sum exp(scale * Q K^T + mask)
+ *
+ * The operation is the one stated on the pages this library follows:
+ *  - score Q K^T / sqrt(D) and Softmax(score) V: "SpAtten: Efficient Sparse
+ *    Attention Architecture with Cascade Token and Head Pruning" (review page),
+ *    Background - Attention Mechanism; probability p_i = exp(s_i)/sum_j exp(s_j)
+ *    in its Algorithm Optimization section D (Progressive Quantization);
+ *  - scaled dot-product with sqrt(d_k), softmax weights, weighted sum of V, the
+ *    padding mask (-inf on pad tokens) and the look-ahead mask (self and earlier
+ *    tokens only): the self-attention explainer page (palettepath-it), sections
+ *    on score scaling, softmax normalisation, masking, multi-head attention;
+ *  - local-window attention (each token looks at its neighbours) and
+ *    variable-length padding: the O(n^2) tutorial page (devhandbook),
+ *    "Local Window Attention" and Example 7;
+ *  - grouped-query and sliding-window attention as named variants:
+ *    "Attentions Under the Microscope" summary page, Methodology;
+ *  - the problem statement Q, K, V in R^{N x d} -> O: the FlashAttention-3
+ *    review page (deepmi.me), input data of the core algorithm;
+ *  - the one-token generation step against a growing K/V cache: the SpAtten
+ *    review, Background - Attention-Based NLP Models (generation stage).
+ *
+ * Layout (all buffers contiguous, innermost dimension last, the
+ * [batch, heads, n, d] order of the tutorial page's SDPA example):
+ *   q, o : [B, Hq,  Nq, d]      k, v : [B, Hkv, Nk, d]
+ *   lse  : [B, Hq,  Nq]  float32, natural log, scale applied
+ *   seqlens : [B] int32 valid key lengths (right padding), or NULL = all Nk
+ *
+ * Semantics (the readings taken where the pages are silent):
+ *   G = Hq / Hkv; query head h reads K/V head h / G (contiguous groups).
+ *   L_b = clamp(seqlens[b], 0, Nk).  If Nq == Nk the first L_b query rows are
+ *   live and row i sits at position i; if Nq == 1 the single query is the last
+ *   token and sits at position L_b - 1 (it sees its own key).
+ *   Query row i may attend to key j iff i is live, j < L_b,
+ *   (causal == 0 or j <= pos(i)) and (window <= 0 or pos(i) - j < window).
+ *   Masked scores are excluded exactly (-inf), never a finite penalty.
+ *   A row with no allowed key (dead padding rows included) gets O = 0 and
+ *   lse = -inf.  Padded K/V/Q contents are never read into a result; they may
+ *   hold NaN.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the
+ * library writes only o and lse.  The decode path (Nq == 1) uses a
+ * library-owned device workspace per device, allocated on first use (and
+ * grown when a larger problem arrives) and released by attn_release().
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ * and never synchronise.  Two concurrent decode calls on one device share the
+ * workspace and must be ordered by the caller (same stream).
+ *
+ * Errors: the return value is a status.  Argument checks run on the host
+ * before any HIP call, so they are testable without a GPU.  No call aborts or
+ * throws.  attn_last_error() describes the most recent non-OK status of the
+ * calling thread.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum miattn_status {
+  MIATTN_OK = 0,
+  MIATTN_ERR_INVALID = -1,      /* null pointer, size <= 0, Hq % Hkv != 0,
+                                   Nq > Nk, window < 0, non-finite scale,
+                                   pointer not 16-byte aligned, size overflow */
+  MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; window > 0 without
+                                   causal; Nq not in {1, Nk} */
+  MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
+  MIATTN_ERR_NOMEM = -4         /* the decode workspace could not be grown */
+};
+
+/* bf16 q, k, v, o (raw 16-bit bfloat16 storage); float32 lse (may be NULL:
+ * not written); int32 seqlens on the device (may be NULL).  Nq == Nk runs the
+ * tiled MFMA prefill kernel; Nq == 1 runs the split-K decode kernel followed
+ * by the log-sum-exp combine kernel. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int window, const int* seqlens, void* stream);
+
+/* Same contract with float32 q, k, v, o; fp32 arithmetic end to end. */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                 float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, int window, const int* seqlens,
+                 void* stream);
+
+/* Message for the calling thread's most recent non-OK status ("" if none).
+ * The pointer stays valid until the thread's next failing call. */
+const char* attn_last_error(void);
+
+/* Frees the library-owned decode workspace on every device that has one.
+ * The caller must ensure no decode call is still running. */
+void attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

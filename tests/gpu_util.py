@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: run libmiattn through its binding on
+seeded inputs and compare with the fp64 oracle to the stated tolerances.
+
+Tolerances (fp32: the stated bar; bf16: the stated bar for bf16 inputs with
+fp32 accumulation):
+  fp32 : max |o - ref| <= 1e-5,              |lse - ref| <= 1e-5
+  bf16 : max |o - ref| <= 2e-2 and sum|o - ref| / sum|ref| <= 1e-2 over live
+         rows,                               |lse - ref| <= 1e-3
+Rows with no allowed key must be exactly o = 0 and lse = -inf on both sides.
+"""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import transformer_self_attention_attn_amd as mi
+
+DEV = torch.device("cuda:0")
+
+TOL = {
+    "fp32": dict(max_abs=1e-5, rel_l1=None, lse=1e-5),
+    "bf16": dict(max_abs=2e-2, rel_l1=1e-2, lse=1e-3),
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x):
+    sl = None
+    if x["seqlens"] is not None:
+        sl = torch.from_numpy(x["seqlens"]).to(DEV)
+    return x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), sl
+
+
+def run_gpu(w, x, *, scale=None, causal=None, window=None, dev_inputs=None):
+    q, k, v, sl = dev_inputs if dev_inputs is not None else to_dev(x)
+    o, lse = mi.attn(q, k, v,
+                     causal=w.causal if causal is None else causal,
+                     window=w.window if window is None else window,
+                     seqlens=sl, scale=w.scale if scale is None else scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def host(o, lse):
+    return (o.float().cpu().numpy().astype(np.float64),
+            lse.cpu().numpy().astype(np.float64))
+
+
+def compare(name, dtype, got_o, got_l, ref_o, ref_l):
+    """Element-wise comparison of matching rows (any leading shape)."""
+    tol = TOL[dtype]
+    live = np.isfinite(ref_l)
+    dead = ~live
+    assert np.array_equal(np.isneginf(got_l), dead), \
+        f"{name}: empty-row pattern differs"
+    assert np.all(got_o[dead] == 0), f"{name}: empty rows not zero"
+    assert np.all(np.isfinite(got_o)), f"{name}: non-finite output"
+    if not live.any():
+        return dict(max_abs=0.0, rel_l1=0.0, lse=0.0)
+    err = np.abs(got_o[live] - ref_o[live])
+    max_abs = float(err.max())
+    rel = float(err.sum() / max(np.abs(ref_o[live]).sum(), 1e-300))
+    lse_err = float(np.abs(got_l[live] - ref_l[live]).max())
+    say(f"  {name}: max_abs={max_abs:.3e} rel_l1={rel:.3e} "
+        f"lse_err={lse_err:.3e} rows={int(live.sum())}/{live.size}")
+    assert max_abs <= tol["max_abs"], f"{name}: max_abs {max_abs}"
+    if tol["rel_l1"] is not None:
+        assert rel <= tol["rel_l1"], f"{name}: rel_l1 {rel}"
+    assert lse_err <= tol["lse"], f"{name}: lse error {lse_err}"
+    return dict(max_abs=max_abs, rel_l1=rel, lse=lse_err)
+
+
+def check_full(name, w, seed, **over):
+    """All rows against the oracle (sizes where the oracle takes seconds)."""
+    say(f"[gpu] {name} seed={seed} shape=B{w.B} Hq{w.Hq} Hkv{w.Hkv} "
+        f"Nq{w.Nq} Nk{w.Nk} d{w.d} {w.dtype} causal={w.causal} "
+        f"window={w.window} padded={w.padded} {over}")
+    x = synth.make_inputs(w, seed)
+    o, lse = run_gpu(w, x, **over)
+    go, gl = host(o, lse)
+    ro, rl = oracle.attention(
+        x["q32"], x["k32"], x["v32"],
+        scale=over.get("scale", w.scale),
+        causal=over.get("causal", w.causal),
+        window=over.get("window", w.window), seqlens=x["seqlens"])
+    return compare(name, w.dtype, go, gl, ro, rl)
+
+
+def sample_rows(w, seqlens, rng, n_random=160):
+    """Rows for a sampled check: tile edges, the ragged tail, the valid-length
+    boundary and random rows."""
+    picks = set()
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, w.Nq // 2, w.Nq - 2,
+             w.Nq - 1]
+    for b in {0, w.B - 1}:
+        for h in {0, w.Hq - 1, w.Hq // 2}:
+            for i in edges:
+                if 0 <= i < w.Nq:
+                    picks.add((b, h, i))
+            if seqlens is not None and w.Nq == w.Nk:
+                L = int(seqlens[b])
+                for i in (L - 2, L - 1, L, L + 1):
+                    if 0 <= i < w.Nq:
+                        picks.add((b, h, i))
+    for _ in range(n_random):
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)),
+                   int(rng.integers(w.Nq))))
+    return sorted(picks)
+
+
+def check_sampled(name, w, seed, x=None, o_lse=None):
+    """Full-size run, sampled rows against the oracle row by row."""
+    say(f"[gpu] {name} (full size, sampled rows) seed={seed}")
+    if x is None:
+        x = synth.make_inputs(w, seed)
+    if o_lse is None:
+        o_lse = run_gpu(w, x)
+    o, lse = o_lse
+    rng = np.random.default_rng(seed + 1000)
+    picks = sample_rows(w, x["seqlens"], rng)
+    idx = tuple(np.array(picks).T)
+    go = o[idx].float().cpu().numpy().astype(np.float64)
+    gl = lse[idx].cpu().numpy().astype(np.float64)
+    ro, rl = oracle.attention_rows(x["q32"], x["k32"], x["v32"], picks,
+                                   scale=w.scale, causal=w.causal,
+                                   window=w.window, seqlens=x["seqlens"])
+    return compare(name, w.dtype, go, gl, ro, rl)
+
+
+def finite_scale(d):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,95 @@
+"""CPU-only: the C-ABI library loads, exports what include/miattn.h declares,
+and rejects bad arguments on the host before any HIP call."""
+
+import os
+import re
+
+import pytest
+
+import transformer_self_attention_attn_amd as mi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "miattn.h")
+
+# fake, 16-byte aligned device addresses: validation must reject the call
+# before anything dereferences them
+P = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mi.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def good(**over):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=64, Nk=64, d=64,
+             scale=0.125, causal=1, window=0, seqlens=0, stream=0)
+    a.update(over)
+    return a
+
+
+def call(fn, a):
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+              a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+              a["window"], a["seqlens"], a["stream"])
+
+
+BAD = [
+    (dict(q=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(v=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(o=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(B=0), mi.MIATTN_ERR_INVALID, "positive"),
+    (dict(Hq=-1), mi.MIATTN_ERR_INVALID, "positive"),
+    (dict(Nk=0), mi.MIATTN_ERR_INVALID, "positive"),
+    (dict(d=0), mi.MIATTN_ERR_INVALID, "positive"),
+    (dict(Hq=6, Hkv=4), mi.MIATTN_ERR_INVALID, "multiple"),
+    (dict(Nq=65), mi.MIATTN_ERR_INVALID, "exceeds"),
+    (dict(window=-1), mi.MIATTN_ERR_INVALID, "negative"),
+    (dict(scale=float("nan")), mi.MIATTN_ERR_INVALID, "finite"),
+    (dict(scale=float("inf")), mi.MIATTN_ERR_INVALID, "finite"),
+    (dict(q=P + 2), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(lse=P + 4), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(d=96), mi.MIATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(d=256), mi.MIATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(window=8, causal=0), mi.MIATTN_ERR_UNSUPPORTED, "causal"),
+    (dict(Nq=32), mi.MIATTN_ERR_UNSUPPORTED, "decode"),
+    (dict(B=70000, Nq=1), mi.MIATTN_ERR_INVALID, "65535"),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 12, Nk=1 << 12),
+     mi.MIATTN_ERR_INVALID, "too large"),
+]
+
+
+@pytest.mark.parametrize("fn_name", ["attn_fwd", "attn_fwd_f32"])
+@pytest.mark.parametrize("over,code,msg", BAD,
+                         ids=[str(b[0]) for b in BAD])
+def test_rejected_on_host(fn_name, over, code, msg):
+    fn = getattr(mi, fn_name)
+    rc = call(fn, good(**over))
+    assert rc == code
+    err = mi.attn_last_error()
+    assert fn_name in err and msg in err, err
+
+
+def test_lse_may_be_null_and_still_validated():
+    rc = call(mi.attn_fwd, good(lse=0, d=80))
+    assert rc == mi.MIATTN_ERR_UNSUPPORTED
+
+
+def test_torch_wrapper_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mi.attn(q, q, q)
+    with pytest.raises(TypeError):
+        mi.attn(q, q, q.float())

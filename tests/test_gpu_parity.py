@@ -1,0 +1,201 @@
+"""GPU parity: libmiattn (through its C ABI) against the fp64 oracle.
+
+Reduced sizes compare every row and span several 128-row query blocks and
+64-key tiles with ragged tails; the five workloads run at full size with
+sampled rows (config 2 and the fp32 case compare every row).  Edge cases:
+empty sequences, one valid key, window of one, N below one tile, GQA groups
+of 1, 2, 4, 7 and 16, negative and zero scale, NaN in the padding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+PREFILL_CASES = [
+    W("mha-d64-nocausal-ragged", 2, 4, 4, 300, 300, 64, "bf16", False),
+    W("mha-d128-nocausal-ragged", 2, 4, 4, 300, 300, 128, "bf16", False),
+    W("gqa3-d64-causal-padded", 3, 6, 2, 333, 333, 64, "bf16", True,
+      len_lo=1, len_hi=333),
+    W("mqa7-d128-causal", 2, 7, 1, 257, 257, 128, "bf16", True),
+    W("gqa2-d64-window64", 2, 4, 2, 700, 700, 64, "bf16", True, window=64),
+    W("d128-window1-self-only", 1, 2, 2, 130, 130, 128, "bf16", True,
+      window=1),
+    W("d64-window1024-long", 1, 2, 2, 2000, 2000, 64, "bf16", True,
+      window=1024),
+    W("d128-below-one-tile-padded", 3, 2, 1, 17, 17, 128, "bf16", True,
+      len_lo=0, len_hi=17),
+    W("d64-exact-tile", 1, 1, 1, 128, 128, 64, "bf16", True),
+    W("gqa4-d128-window100-padded", 2, 8, 2, 515, 515, 128, "bf16", True,
+      window=100, len_lo=60, len_hi=515),
+    W("amp3-d128-causal", 1, 2, 1, 200, 200, 128, "bf16", True, amp=3.0),
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_CASES, ids=lambda w: w.name)
+def test_prefill_small(w):
+    for seed in (11, 12):
+        gu.check_full(w.name, w, seed)
+
+
+DECODE_CASES = [
+    W("decode-gqa4-d128-padded", 6, 8, 2, 1, 3000, 128, "bf16", True,
+      len_lo=0, len_hi=3000),
+    W("decode-mha-d64-full", 2, 4, 4, 1, 1100, 64, "bf16", True),
+    W("decode-window100", 4, 8, 2, 1, 2100, 128, "bf16", True, window=100,
+      len_lo=1, len_hi=2100),
+    W("decode-gqa7-d64", 3, 14, 2, 1, 777, 64, "bf16", True, len_lo=1,
+      len_hi=777),
+    W("decode-mqa16-d128", 2, 16, 1, 1, 1025, 128, "bf16", True,
+      len_lo=500, len_hi=1025),
+    W("decode-nocausal", 2, 8, 2, 1, 600, 128, "bf16", False, len_lo=1,
+      len_hi=600),
+    W("decode-one-key", 2, 4, 1, 1, 1, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: w.name)
+def test_decode_small(w):
+    for seed in (21, 22):
+        gu.check_full(w.name, w, seed)
+
+
+def test_decode_chunk_boundaries():
+    """Valid lengths on and around the 512-key split boundaries."""
+    w = W("decode-boundaries", 8, 4, 1, 1, 2048, 128, "bf16", True,
+          len_lo=1, len_hi=2048)
+    x = synth.make_inputs(w, 31)
+    x["seqlens"] = np.array([1, 511, 512, 513, 1024, 1025, 2047, 2048],
+                            dtype=np.int32)
+    q, k, v, sl = gu.to_dev(x)
+    o, lse = gu.run_gpu(w, x, dev_inputs=(q, k, v, sl))
+    go, gl = gu.host(o, lse)
+    import oracle
+    ro, rl = oracle.attention(x["q32"], x["k32"], x["v32"], scale=w.scale,
+                              causal=True, seqlens=x["seqlens"])
+    gu.compare(w.name, "bf16", go, gl, ro, rl)
+
+
+FP32_CASES = [
+    W("fp32-gqa-causal-padded-d128", 2, 4, 2, 150, 150, 128, "fp32", True,
+      len_lo=1, len_hi=150),
+    W("fp32-window-d64", 1, 2, 1, 200, 200, 64, "fp32", True, window=17),
+    W("fp32-decode-d64", 3, 4, 2, 1, 300, 64, "fp32", True, len_lo=0,
+      len_hi=300),
+]
+
+
+@pytest.mark.parametrize("w", FP32_CASES, ids=lambda w: w.name)
+def test_fp32_small(w):
+    gu.check_full(w.name, w, 41)
+
+
+def test_scale_zero_and_negative():
+    w = W("scale-edge", 2, 4, 2, 190, 190, 128, "bf16", True, len_lo=50,
+          len_hi=190)
+    gu.check_full("scale-zero", w, 51, scale=0.0)
+    gu.check_full("scale-negative", w, 52, scale=-0.2)
+    wn = W("scale-negative-nocausal", 1, 2, 2, 150, 150, 64, "bf16", False)
+    gu.check_full(wn.name, wn, 53, scale=-0.3)
+    wd = W("decode-scale-zero", 2, 4, 2, 1, 700, 128, "bf16", True,
+           len_lo=1, len_hi=700)
+    gu.check_full(wd.name, wd, 54, scale=0.0)
+
+
+# ---- the five workloads at full size ----------------------------------------
+
+def test_config_fp32_single_head():
+    w = synth.by_name("fp32-single-head")
+    for seed in (1, 101, 201):
+        gu.check_full(w.name, w, seed)
+
+
+def test_config_gpt2_small_causal_padded_all_rows():
+    w = synth.by_name("gpt2-small-causal-padded")
+    gu.check_full(w.name, w, 2)
+
+
+@pytest.mark.parametrize("name,seed", [
+    ("gpt2-small-causal-padded", 102),
+    ("gqa-causal-prefill", 3),
+    ("gqa-causal-prefill", 103),
+    ("sliding-window-causal", 4),
+    ("decode-gqa", 5),
+    ("decode-gqa", 105),
+])
+def test_config_full_size_sampled(name, seed):
+    w = synth.by_name(name)
+    gu.check_sampled(name, w, seed)
+
+
+# ---- robustness and invariants ----------------------------------------------
+
+@pytest.mark.parametrize("w", [
+    W("nan-pad-prefill", 3, 4, 2, 300, 300, 128, "bf16", True, len_lo=1,
+      len_hi=300),
+    W("nan-pad-decode", 4, 8, 2, 1, 1300, 128, "bf16", True, len_lo=1,
+      len_hi=1300),
+    W("nan-pad-fp32", 2, 2, 1, 100, 100, 64, "fp32", True, len_lo=1,
+      len_hi=100),
+], ids=lambda w: w.name)
+def test_nan_padding_is_never_read(w):
+    gu.say(f"[gpu] {w.name}")
+    a = synth.make_inputs(w, 61, pad_fill="draw")
+    b = synth.make_inputs(w, 61, pad_fill="nan")
+    oa, la = gu.run_gpu(w, a)
+    ob, lb = gu.run_gpu(w, b)
+    assert torch.isfinite(ob.float()).all()
+    assert torch.equal(oa, ob)
+    assert torch.equal(la, lb)
+
+
+def test_deterministic_bitwise():
+    for w in (W("det-prefill", 2, 8, 2, 520, 520, 128, "bf16", True),
+              W("det-decode", 4, 8, 2, 1, 2000, 128, "bf16", True, len_lo=1,
+                len_hi=2000)):
+        x = synth.make_inputs(w, 71)
+        dev = gu.to_dev(x)
+        o1, l1 = gu.run_gpu(w, x, dev_inputs=dev)
+        o2, l2 = gu.run_gpu(w, x, dev_inputs=dev)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_equals_repeated_mha_bitwise():
+    w = W("gqa", 2, 6, 2, 300, 300, 128, "bf16", True, len_lo=100,
+          len_hi=300)
+    x = synth.make_inputs(w, 81)
+    q, k, v, sl = gu.to_dev(x)
+    og, lg = gu.run_gpu(w, x, dev_inputs=(q, k, v, sl))
+    kr = k.repeat_interleave(3, dim=1).contiguous()
+    vr = v.repeat_interleave(3, dim=1).contiguous()
+    wm = w.with_(Hkv=6)
+    om, lm = gu.run_gpu(wm, x, dev_inputs=(q, kr, vr, sl))
+    assert torch.equal(og, om) and torch.equal(lg, lm)
+
+
+def test_window_n_equals_causal_bitwise():
+    w = W("win", 2, 4, 2, 333, 333, 64, "bf16", True)
+    x = synth.make_inputs(w, 91)
+    dev = gu.to_dev(x)
+    oc, lc = gu.run_gpu(w, x, dev_inputs=dev)
+    for win in (333, 5000):
+        ow, lw = gu.run_gpu(w, x, dev_inputs=dev, window=win)
+        assert torch.equal(oc, ow) and torch.equal(lc, lw)
+
+
+def test_v_ones_gives_ones():
+    w = W("vones", 2, 4, 2, 260, 260, 128, "bf16", True, len_lo=1,
+          len_hi=260, amp=2.0)
+    x = synth.make_inputs(w, 95)
+    q, k, v, sl = gu.to_dev(x)
+    v1 = torch.ones_like(v)
+    o, lse = gu.run_gpu(w, x, dev_inputs=(q, k, v1, sl))
+    live = torch.isfinite(lse)
+    assert (o.float()[live] - 1).abs().max().item() <= 8e-3
+    assert (o.float()[~live] == 0).all()

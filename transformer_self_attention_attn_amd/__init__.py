@@ -1,0 +1,126 @@
+"""Python binding of libmiattn (argument marshalling only).
+
+Every step of attention runs in the HIP kernels of libmiattn.so; this module
+only turns torch tensors into device pointers, sizes and the current HIP
+stream, and raises on a non-OK status.  There is no fallback: if the library
+is not built, importing the binding's entry points raises.
+
+Entry points with the C names (raw pointers as Python ints):
+    attn_fwd, attn_fwd_f32, attn_last_error, attn_release
+Convenience wrapper on torch tensors:
+    attn(q, k, v, causal=False, window=0, seqlens=None, scale=None)
+"""
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmiattn.so")
+
+MIATTN_OK = 0
+MIATTN_ERR_INVALID = -1
+MIATTN_ERR_UNSUPPORTED = -2
+MIATTN_ERR_HIP = -3
+MIATTN_ERR_NOMEM = -4
+
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_last_error", "attn_release")
+
+_lib = None
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"miattn status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libmiattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, vp]
+    lib.attn_fwd.argtypes = sig
+    lib.attn_fwd.restype = ci
+    lib.attn_fwd_f32.argtypes = sig
+    lib.attn_fwd_f32.restype = ci
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_release.argtypes = []
+    lib.attn_release.restype = None
+    _lib = lib
+    return lib
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+             seqlens, stream):
+    """Direct call of the C entry point; pointers are ints (0 = NULL)."""
+    return load().attn_fwd(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nk, d,
+                           scale, int(causal), window, seqlens or None,
+                           stream or None)
+
+
+def attn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 window, seqlens, stream):
+    return load().attn_fwd_f32(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nk,
+                               d, scale, int(causal), window, seqlens or None,
+                               stream or None)
+
+
+def attn_last_error():
+    return load().attn_last_error().decode()
+
+
+def attn_release():
+    load().attn_release()
+
+
+def attn(q, k, v, *, causal=False, window=0, seqlens=None, scale=None,
+         out=None, lse=None, stream=None):
+    """Attention on torch device tensors.
+
+    q: [B, Hq, Nq, d], k/v: [B, Hkv, Nk, d], all bfloat16 or all float32,
+    contiguous, on the same GPU.  seqlens: int32 device tensor [B] or None.
+    Returns (o, lse) with o like q and lse float32 [B, Hq, Nq].  The default
+    scale is 1/sqrt(d).
+    """
+    import torch
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-d GPU tensors")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("shape mismatch between q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    sl = 0
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or not seqlens.is_cuda or \
+                seqlens.numel() != B:
+            raise ValueError("seqlens must be an int32 GPU tensor of size B")
+        sl = seqlens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), causal,
+            int(window), sl, stream)
+    if rc != MIATTN_OK:
+        raise MiattnError(rc, attn_last_error())
+    return out, lse

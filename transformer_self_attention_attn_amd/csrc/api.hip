@@ -1,0 +1,187 @@
+// C-ABI layer of libmiattn: argument validation (host only, before any HIP
+// call), dispatch to the kernels, the decode workspace and error reporting.
+// The contract is documented in include/miattn.h.
+#include "miattn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Shared checks of attn_fwd and attn_fwd_f32.  No HIP call happens here.
+int validate(const char* fn, const void* q, const void* k, const void* v,
+             const void* o, const float* lse, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, float scale, int causal, int window) {
+  if (!q || !k || !v || !o)
+    return fail(MIATTN_ERR_INVALID, "%s: q, k, v and o must be non-null", fn);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return fail(MIATTN_ERR_INVALID,
+                "%s: sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d "
+                "d=%d)",
+                fn, B, Hq, Hkv, Nq, Nk, d);
+  if (Hq % Hkv != 0)
+    return fail(MIATTN_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d",
+                fn, Hq, Hkv);
+  if (Nq > Nk)
+    return fail(MIATTN_ERR_INVALID, "%s: Nq=%d exceeds Nk=%d", fn, Nq, Nk);
+  if (window < 0)
+    return fail(MIATTN_ERR_INVALID, "%s: window=%d is negative", fn, window);
+  if (!std::isfinite(scale))
+    return fail(MIATTN_ERR_INVALID, "%s: scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return fail(MIATTN_ERR_INVALID,
+                "%s: q, k, v, o and lse must be 16-byte aligned", fn);
+  if (d != 64 && d != 128)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: head dim d=%d (supported: 64, 128)",
+                fn, d);
+  if (window > 0 && !causal)
+    return fail(MIATTN_ERR_UNSUPPORTED,
+                "%s: a window needs the causal mask (one-sided look-back)", fn);
+  if (Nq != 1 && Nq != Nk)
+    return fail(MIATTN_ERR_UNSUPPORTED,
+                "%s: Nq=%d must be 1 (decode) or Nk=%d (prefill)", fn, Nq, Nk);
+  // index arithmetic bounds: element offsets are 64-bit, row and block
+  // counts are 32-bit, decode grid y/z are limited to 65535
+  const long long qrows = (long long)B * Hq * Nq;
+  const long long qblocks = (long long)B * Hq * ((Nq + 127) / 128);
+  if (qrows > 0x7fffffffLL || qblocks > 0x7fffffffLL ||
+      (long long)B * Hkv * Nk > 0x7fffffffLL)
+    return fail(MIATTN_ERR_INVALID, "%s: problem too large for one launch",
+                fn);
+  if (Nq == 1 && (B > 65535 || Hq > 65535))
+    return fail(MIATTN_ERR_INVALID, "%s: decode needs B and Hq <= 65535", fn);
+  return MIATTN_OK;
+}
+
+// ---- decode workspace, one per device -------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mu;
+void* g_ws[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+int workspace(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MIATTN_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws[dev]) {
+      e = hipFree(g_ws[dev]);  // waits for work still using it
+      g_ws[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+      if (e != hipSuccess)
+        return fail(MIATTN_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    e = hipMalloc(&g_ws[dev], need);
+    if (e != hipSuccess) {
+      g_ws[dev] = nullptr;
+      (void)hipGetLastError();
+      return fail(MIATTN_ERR_NOMEM, "decode workspace of %zu bytes: %s", need,
+                  hipGetErrorString(e));
+    }
+    g_ws_bytes[dev] = need;
+  }
+  *out = g_ws[dev];
+  return MIATTN_OK;
+}
+
+miattn::Problem make_problem(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                             float scale, int causal, int window,
+                             const int* seqlens) {
+  miattn::Problem p;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  p.window = window;
+  p.seqlens = seqlens;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int window, const int* seqlens, void* stream) {
+  int rc = validate("attn_fwd", q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                    causal, window);
+  if (rc != MIATTN_OK) return rc;
+  const miattn::Problem p =
+      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, seqlens);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (Nq == 1) {
+    void* ws = nullptr;
+    rc = workspace(miattn::decode_workspace_bytes(p), &ws);
+    if (rc != MIATTN_OK) return rc;
+    e = miattn::launch_decode_bf16(q, k, v, o, lse, p, ws, st);
+  } else {
+    e = miattn::launch_prefill_bf16(q, k, v, o, lse, p, st);
+  }
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "attn_fwd launch: %s", hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                 float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, int window, const int* seqlens,
+                 void* stream) {
+  const int rc = validate("attn_fwd_f32", q, k, v, o, lse, B, Hq, Hkv, Nq, Nk,
+                          d, scale, causal, window);
+  if (rc != MIATTN_OK) return rc;
+  const miattn::Problem p =
+      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, seqlens);
+  const hipError_t e = miattn::launch_attn_f32(
+      q, k, v, o, lse, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "attn_fwd_f32 launch: %s",
+                hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+void attn_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    if (!g_ws[dev]) continue;
+    if (hipSetDevice(dev) == hipSuccess) (void)hipFree(g_ws[dev]);
+    g_ws[dev] = nullptr;
+    g_ws_bytes[dev] = 0;
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

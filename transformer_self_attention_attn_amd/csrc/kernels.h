@@ -1,0 +1,36 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+// Not installed; callers use include/miattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace miattn {
+
+// One attention problem, already validated by the C-ABI layer.
+struct Problem {
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal, window;
+  const int* seqlens;  // device pointer or nullptr
+};
+
+// Tiled bf16 MFMA prefill (Nq == Nk).
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
+                               void* o, float* lse, const Problem& p,
+                               hipStream_t stream);
+
+// Split-K bf16 decode (Nq == 1) and its log-sum-exp combine.  `ws` must hold
+// decode_workspace_bytes(p) bytes.
+size_t decode_workspace_bytes(const Problem& p);
+hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
+                              void* o, float* lse, const Problem& p, void* ws,
+                              hipStream_t stream);
+
+// fp32 path (any Nq in {1, Nk}).
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v,
+                           float* o, float* lse, const Problem& p,
+                           hipStream_t stream);
+
+}  // namespace miattn
