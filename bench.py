@@ -93,9 +93,9 @@ def traffic_for(kind):
 
 
 def cpu_baseline(w, x, budget_s=20.0):
-    """Times the fp64 oracle (as it stands) on whole heads of batch 0 of the
-    prefill workload until about `budget_s` seconds of CPU work are done."""
-    import numpy as np
+    """Times the fp64 oracle (as it stands) on whole (batch, head) slices of
+    the prefill workload, in order, until about `budget_s` seconds of CPU
+    work are done; reports algorithmic TFLOP/s of that sample."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -104,26 +104,26 @@ def cpu_baseline(w, x, budget_s=20.0):
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = 1
     q32, k32, v32 = x["q32"], x["k32"], x["v32"]
-    heads_done = 0
+    done = 0
     t_total = 0.0
     per_head_pairs = allowed_pairs(w.with_(B=1), None)
     g = w.Hq // w.Hkv
-    while t_total < budget_s and heads_done < w.Hq:
-        h = heads_done
+    while t_total < budget_s and done < w.B * w.Hq:
+        b, h = divmod(done, w.Hq)
         hk = h // g
         t0 = time.perf_counter()
-        oracle.attention(q32[:1, h:h + 1], k32[:1, hk:hk + 1],
-                         v32[:1, hk:hk + 1], scale=w.scale, causal=w.causal,
-                         window=w.window, seqlens=None)
+        oracle.attention(q32[b:b + 1, h:h + 1], k32[b:b + 1, hk:hk + 1],
+                         v32[b:b + 1, hk:hk + 1], scale=w.scale,
+                         causal=w.causal, window=w.window, seqlens=None)
         t_total += time.perf_counter() - t0
-        heads_done += 1
-    flops = 4.0 * w.d * per_head_pairs * heads_done
+        done += 1
+    flops = 4.0 * w.d * per_head_pairs * done
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
-            "sample": (f"{heads_done} of {w.B * w.Hq} (batch, head) slices "
-                       f"of {w.name} (batch 0, all {w.Nq} query rows each), "
-                       f"{t_total:.1f} s, fp64 NumPy"),
-            "seconds": t_total}
+            "sample": (f"{done} of {w.B * w.Hq} (batch, head) slices of "
+                       f"{w.name}, all {w.Nq} query rows each, "
+                       f"{t_total:.1f} s of fp64 NumPy"),
+            "seconds": round(t_total, 2)}
 
 
 def main():

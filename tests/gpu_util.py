@@ -7,6 +7,9 @@ fp32 accumulation):
   bf16 : max |o - ref| <= 2e-2 and sum|o - ref| / sum|ref| <= 1e-2 over live
          rows,                               |lse - ref| <= 1e-3
 Rows with no allowed key must be exactly o = 0 and lse = -inf on both sides.
+The absolute bound is stated for unit-scale inputs; for an edge case whose V
+is drawn with amplitude a > 1 the output (and its bf16 rounding) scales with a,
+so the absolute bound is multiplied by a (the relative bound is unchanged).
 """
 
 import math
@@ -54,9 +57,10 @@ def host(o, lse):
             lse.cpu().numpy().astype(np.float64))
 
 
-def compare(name, dtype, got_o, got_l, ref_o, ref_l):
+def compare(name, dtype, got_o, got_l, ref_o, ref_l, vmag=1.0):
     """Element-wise comparison of matching rows (any leading shape)."""
-    tol = TOL[dtype]
+    tol = dict(TOL[dtype])
+    tol["max_abs"] *= max(1.0, vmag)
     live = np.isfinite(ref_l)
     dead = ~live
     assert np.array_equal(np.isneginf(got_l), dead), \
@@ -91,7 +95,7 @@ def check_full(name, w, seed, **over):
         scale=over.get("scale", w.scale),
         causal=over.get("causal", w.causal),
         window=over.get("window", w.window), seqlens=x["seqlens"])
-    return compare(name, w.dtype, go, gl, ro, rl)
+    return compare(name, w.dtype, go, gl, ro, rl, vmag=w.amp)
 
 
 def sample_rows(w, seqlens, rng, n_random=160):
@@ -132,7 +136,7 @@ def check_sampled(name, w, seed, x=None, o_lse=None):
     ro, rl = oracle.attention_rows(x["q32"], x["k32"], x["v32"], picks,
                                    scale=w.scale, causal=w.causal,
                                    window=w.window, seqlens=x["seqlens"])
-    return compare(name, w.dtype, go, gl, ro, rl)
+    return compare(name, w.dtype, go, gl, ro, rl, vmag=w.amp)
 
 
 def finite_scale(d):

@@ -161,10 +161,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       for (int gi = 0; gi < GB; ++gi) {
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e) {
+          // copy the vector element out first: bit-casting the element
+          // expression itself would read element 0
+          const unsigned kw = kk[u][e];
+          const unsigned qv = qw[gi][e];
           acc = __builtin_amdgcn_fdot2_f32_bf16(
-              __builtin_bit_cast(bf16x2, kk[u][e]),
-              __builtin_bit_cast(bf16x2, qw[gi][e]), acc, false);
+              __builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qv),
+              acc, false);
+        }
         acc = group_sum<LPK>(acc);
         if (dch == 0)
           sc[(key - c0) * GB + gi] = ok ? acc * p.c : -INFINITY;
