@@ -24,6 +24,18 @@
 //   block index is remapped so that each XCD (own L2) works on a contiguous
 //   range of (batch, K/V head) groups; causal blocks run heaviest first.
 //
+// Data movement
+//   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
+//   loads (no register staging).  Rows past the valid length are loaded from
+//   a 16-byte block of zeros instead, so padded contents never enter LDS.
+//   LDS rows are padded (K: +16 B, V: +64 B per row); with those strides every
+//   matrix-operand read below touches each LDS bank once, and every operand
+//   address is a per-lane base plus a compile-time offset.  K rows are stored
+//   in the order the 32x32 MFMA wants (see k_row_key); V keeps its natural
+//   [key][d] order and is read with the transposing LDS read
+//   ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
+//   column, exactly the A operand of V^T.
+//
 // Per tile, per wave (the transposed formulation keeps each query's softmax
 // statistics inside one lane pair):
 //   S^T[key][query] = K_tile . Q^T     v_mfma_f32_32x32x16_bf16, A = K rows
@@ -32,11 +44,14 @@
 //   running maximum is only moved (and O rescaled) when some row's new
 //   maximum exceeds it by more than 2^8, which is exact arithmetic: the
 //   stored maximum is any common shift of the row's scores
-//   O^T[d][query] += V^T . P^T         A = V^T from LDS (V is transposed on
-//                                      its way into LDS), B = P^T (bf16) taken
-//                                      straight from the S^T accumulator
-// K/V tiles are double-buffered in LDS and the next tile's global loads are
-// issued before the current tile's matrix work.
+//   O^T[d][query] += V^T . P^T         A = V^T via transposing LDS reads,
+//                                      B = P^T (bf16) taken straight from
+//                                      the S^T accumulator
+// Two-stage software pipeline: while the softmax of tile t runs on the
+// vector ALUs, the S^T product of tile t+1 is already issued to the matrix
+// cores.  K is therefore staged one tile ahead of V; the LDS ring holds
+// K(t+1), K(t+2) and V(t), V(t+1), and the loads of the next tiles are in
+// flight during a whole tile of work.
 #include "kernels.h"
 
 #include <cmath>
@@ -48,8 +63,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -59,20 +74,34 @@ constexpr int kKT = 64;             // keys per tile
 constexpr float kTau = 8.0f;        // lazy-rescale threshold, log2 units
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies
 
+// 16 zero bytes: the source of every direct-to-LDS load of a row past the
+// valid length.
+__device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u,
+                                                                     0u};
+
 template <int D>
 struct Cfg {
-  static constexpr int KSTR = D + 8;      // K tile row stride in LDS (elements)
-  static constexpr int VSTR = kKT + 8;    // V^T tile row stride (elements)
-  static constexpr int KBUF = kKT * KSTR;
-  static constexpr int VBUF = D * VSTR;
-  static constexpr int KCH = kKT * D / 8;             // 16-byte chunks per tile
-  static constexpr int KCH_T = KCH / kThreads;        // per thread
-  static constexpr int VUNITS = (kKT / 4) * (D / 8);  // 4 keys x 8 columns
-  static constexpr int VU_T = (VUNITS + kThreads - 1) / kThreads;
+  static constexpr int KSTR = D + 8;    // K tile row stride (elements)
+  static constexpr int VSTR = D + 32;   // V tile row stride (elements)
+  static constexpr int KSLOTS = KSTR / 8;  // 16-byte slots per K row
+  static constexpr int VSLOTS = VSTR / 8;
+  static constexpr int KTILE = kKT * KSTR;
+  static constexpr int VTILE = kKT * VSTR;
+  static constexpr int KLOADS = kKT * KSLOTS / 64;  // wave-wide 1 KB loads
+  static constexpr int VLOADS = kKT * VSLOTS / 64;
   static constexpr int KS = D / 16;  // k-steps of the S^T product
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
-  static_assert(KCH % kThreads == 0, "K tile split");
+  static_assert(kKT * KSLOTS % 64 == 0 && kKT * VSLOTS % 64 == 0, "split");
 };
+
+// Key held in row r of the K tile in LDS.  Rows are in MFMA row order: with
+// this order the 32x32 accumulator of S^T gives lane group g (lanes 32g ..
+// 32g+31) the 16 consecutive keys g*16 .. g*16+15 of each 32-key block.
+__device__ inline int k_row_key(int r) {
+  const int mb = r >> 5;
+  const int rho = r & 31;
+  return mb * 32 + ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3);
+}
 
 struct PrefillParams {
   const uint16_t* q;
@@ -86,26 +115,14 @@ struct PrefillParams {
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
 };
 
-__device__ inline unsigned perm(unsigned hi_src, unsigned lo_src,
-                                unsigned sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-}
-
-// Row of the K tile in LDS that feeds MFMA row rho of key block mb.  Keys are
-// stored permuted so that, in the 32x32 accumulator layout, lane group g of
-// the S^T result holds the 16 consecutive keys g*16 .. g*16+15 of the block.
-__device__ inline int k_lds_row(int key_in_tile) {
-  const int mb = key_in_tile >> 5;
-  const int kk = key_in_tile & 31;
-  const int rho = ((kk >> 2) & 3) * 8 + ((kk >> 4) & 1) * 4 + (kk & 3);
-  return mb * 32 + rho;
-}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::VBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::VTILE];
 
   // ---- block -> (batch, head, query block) --------------------------------
   const int n = p.total;
@@ -165,7 +182,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int w_hi_max = p.causal ? min(L, wend) : L;
   const int w_hi_min = p.causal ? min(L, qw0 + 1) : L;
   const int w_lo_min = p.window > 0 ? max(0, qw0 - p.window + 1) : 0;
-  const int w_lo_max = p.window > 0 ? max(0, wend - 1 - p.window + 1) : 0;
+  const int w_lo_max = p.window > 0 ? max(0, wend - p.window) : 0;
+  auto wave_needs = [&](int t) {
+    const int j0 = t * kKT;
+    return wlive && j0 < w_hi_max && j0 + kKT > w_lo_min;
+  };
+  auto tile_full = [&](int t) {
+    const int j0 = t * kKT;
+    return j0 >= w_lo_max && j0 + kKT <= w_hi_min;
+  };
 
   // ---- Q^T fragments (B operand), kept in registers -----------------------
   bf16x8 qf[C::KS];
@@ -180,67 +205,100 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // ---- tile staging -------------------------------------------------------
-  u32x4 kr[C::KCH_T];
-  u32x4 vr[4 * C::VU_T];
-  auto gload = [&](int t) {
+  // ---- direct-to-LDS tile loads ---------------------------------------------
+  // Wave-wide load i fills LDS bytes [i * 1024, +1024) of the tile: lane l
+  // writes 16-byte slot i*64 + l, i.e. (row, chunk) of the padded row.  Loads
+  // are dealt round-robin to the four waves; each lane's source offset within
+  // a tile is fixed, so it is computed once.  Pad chunks are never read and
+  // take the row's first chunk.  Only a tile that runs past the valid length
+  // takes the checked path, where such rows read the zero block.
+  constexpr int KLW = (C::KLOADS + kWaves - 1) / kWaves;  // loads per wave
+  constexpr int VLW = (C::VLOADS + kWaves - 1) / kWaves;
+  int koff[KLW], krow_of[KLW], voff[VLW], vrow_of[VLW];
+#pragma unroll
+  for (int n = 0; n < KLW; ++n) {
+    const int slot16 = (wave + kWaves * n) * 64 + lane;
+    const int r = slot16 / C::KSLOTS;
+    const int c = slot16 - r * C::KSLOTS;
+    krow_of[n] = k_row_key(r);
+    koff[n] = krow_of[n] * D + (c < D / 8 ? c * 8 : 0);
+  }
+#pragma unroll
+  for (int n = 0; n < VLW; ++n) {
+    const int slot16 = (wave + kWaves * n) * 64 + lane;
+    const int r = slot16 / C::VSLOTS;
+    const int c = slot16 - r * C::VSLOTS;
+    vrow_of[n] = r;
+    voff[n] = r * D + (c < D / 8 ? c * 8 : 0);
+  }
+  auto dma = [&](const uint16_t* gsrc, uint16_t* lds, const int (&off)[KLW > VLW ? KLW : VLW],
+                 const int (&row)[KLW > VLW ? KLW : VLW], int nloads, int t) {
     const int j0 = t * kKT;
+    const uint16_t* base = gsrc + (size_t)j0 * D;
+    const bool whole = j0 + kKT <= L;
 #pragma unroll
-    for (int i = 0; i < C::KCH_T; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch / (D / 8);
-      const int col = ch % (D / 8);
-      const int key = j0 + row;
-      kr[i] = (key < L) ? *reinterpret_cast<const u32x4*>(
-                              kg + (size_t)key * D + col * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < C::VU_T; ++i) {
-      const int u = tid + kThreads * i;
-      const int kq = u % (kKT / 4);
-      const int dc = u / (kKT / 4);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = j0 + 4 * kq + rr;
-        vr[4 * i + rr] = (u < C::VUNITS && key < L)
-                             ? *reinterpret_cast<const u32x4*>(
-                                   vg + (size_t)key * D + dc * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+    for (int n = 0; n < (KLW > VLW ? KLW : VLW); ++n) {
+      const int i = wave + kWaves * n;
+      if (i < nloads) {
+        const void* src = (whole || j0 + row[n] < L)
+                              ? (const void*)(base + off[n])
+                              : (const void*)kZero16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + i * 512), 16,
+                                         0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  constexpr int LW = KLW > VLW ? KLW : VLW;
+  int koffw[LW], krw[LW], voffw[LW], vrw[LW];
 #pragma unroll
-    for (int i = 0; i < C::KCH_T; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch / (D / 8);
-      const int col = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][k_lds_row(row) * C::KSTR + col * 8]) =
-          kr[i];
-    }
+  for (int n = 0; n < LW; ++n) {
+    koffw[n] = n < KLW ? koff[n] : 0;
+    krw[n] = n < KLW ? krow_of[n] : 0;
+    voffw[n] = n < VLW ? voff[n] : 0;
+    vrw[n] = n < VLW ? vrow_of[n] : 0;
+  }
+  auto dma_k = [&](int t, int buf) {
+    dma(kg, Ks[buf], koffw, krw, C::KLOADS, t);
+  };
+  auto dma_v = [&](int t, int buf) {
+    dma(vg, Vs[buf], voffw, vrw, C::VLOADS, t);
+  };
+
+  // ---- S^T = K . Q^T for one tile -----------------------------------------
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
 #pragma unroll
-    for (int i = 0; i < C::VU_T; ++i) {
-      const int u = tid + kThreads * i;
-      if (u < C::VUNITS) {
-        const int kq = u % (kKT / 4);
-        const int dc = u / (kKT / 4);
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint16_t* krow = &Ks[buf][(mb * 32 + ql) * C::KSTR + 8 * g];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const unsigned a0 = vr[4 * i + 0][cc], a1 = vr[4 * i + 1][cc];
-          const unsigned a2 = vr[4 * i + 2][cc], a3 = vr[4 * i + 3][cc];
-          // column d = dc*8 + 2cc takes the low halves, d + 1 the high halves
-          const u32x2 lo2 = {perm(a1, a0, 0x05040100u),
-                             perm(a3, a2, 0x05040100u)};
-          const u32x2 hi2 = {perm(a1, a0, 0x07060302u),
-                             perm(a3, a2, 0x07060302u)};
-          const int d0 = dc * 8 + 2 * cc;
-          *reinterpret_cast<u32x2*>(&Vs[buf][d0 * C::VSTR + 4 * kq]) = lo2;
-          *reinterpret_cast<u32x2*>(&Vs[buf][(d0 + 1) * C::VSTR + 4 * kq]) =
-              hi2;
-        }
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0,
+                                                        0);
       }
     }
+  };
+
+  // V^T operand: lane i of 16-lane group G reads, for 4 keys at a time, the
+  // column dbase + i; source lane s addresses row key0 + s/4, columns
+  // dbase + 4*(s%4) .. +3.
+  const int grp16 = lane >> 4;
+  const int i16 = lane & 15;
+  const int v_lane = (i16 >> 2) * C::VSTR + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  auto v_operand = [&](int buf, int key0, int db) {
+    bf16x8 a;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint16_t* ptr =
+          &Vs[buf][v_lane + (key0 + 4 * half) * C::VSTR + db * 32];
+      const i16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(ptr));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[4 * half + e] = __builtin_bit_cast(__bf16, (short)r4[e]);
+    }
+    return a;
   };
 
   f32x16 oacc[C::DB];
@@ -251,91 +309,140 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   float M = -INFINITY;  // running maximum of s * c (log2 units)
   float l = 0.f;        // this lane's half of the running sum
 
+  f32x16 sa[2], sb[2];
+
+  // prologue: K(t0), K(t0+1), V(t0) in LDS; S(t0) in registers
   if (t1 > t0) {
-    gload(t0);
-    lstore(0);
+    dma_k(t0, 0);
+    dma_v(t0, 0);
+    if (t0 + 1 < t1) dma_k(t0 + 1, 1);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t1 > t0 && wave_needs(t0)) qk(0, sa);
   __syncthreads();
 
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < t1) gload(t + 1);
+  // One tile of work for a wave, on the scores `sc` of tile t; the S^T
+  // product of tile t+1 is issued into `sn` first, so that its matrix work
+  // overlaps this tile's exponentials (at the end of the range it reads a
+  // stale buffer and the result is dropped).
+  auto tile = [&](int t, int buf, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int j0 = t * kKT;
-    const bool skip = !wlive || j0 >= w_hi_max || j0 + kKT <= w_lo_min;
-    if (!skip) {
-      const bool full = j0 >= w_lo_max && j0 + kKT <= w_hi_min;
-      f32x16 sacc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &Ks[buf][(mb * 32 + ql) * C::KSTR + 16 * ks + 8 * g]);
-          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks],
-                                                             sacc[mb], 0, 0, 0);
-        }
-      }
-      // lane holds keys j0 + mb*32 + g*16 + r (r = 0..15) of query qi
-      if (!full) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + mb * 32 + g * 16 + r;
-            if (j < lo || j >= hi) sacc[mb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float tm = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-      const bool need = tm > M + kTau;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float mn = fmaxf(M, tm);
-        const float alpha =
-            (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        M = mn;
-      }
-      const float mu = (M == -INFINITY) ? 0.f : M;
+    // lane holds keys j0 + mb*32 + g*16 + r (r = 0..15) of query qi
+    if (!tile_full(t)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sacc[mb][r];
-          float e = __builtin_amdgcn_exp2f(fmaf(s, p.c, -mu));
-          if (!full) e = (s == -INFINITY) ? 0.f : e;
-          sacc[mb][r] = e;
-          l += e;
-        }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = sacc[mb][8 * m + e];
-          const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                &Vs[buf][(db * 32 + ql) * C::VSTR + mb * 32 + 16 * g + 8 * m]);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db],
-                                                               0, 0, 0);
-          }
+          const int j = j0 + mb * 32 + g * 16 + r;
+          if (j < lo || j >= hi) sc[mb][r] = -INFINITY;
         }
     }
-    if (t + 1 < t1) lstore(buf ^ 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float tm = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+    const bool need = tm > M + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float mn = fmaxf(M, tm);
+      const float alpha =
+          (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      M = mn;
+    }
+    const float mu = (M == -INFINITY) ? 0.f : M;
+
+    // S^T(t+1) = K(t+1) . Q^T interleaved with this tile's exponentials.
+    // K operand reads run four MFMAs ahead of their use.
+    constexpr int NQK = 2 * C::KS;       // MFMAs of the S^T product
+    constexpr int EPS = 32 / NQK;        // exponentials per MFMA slot
+    const uint16_t* kbase = &Ks[buf ^ 1][ql * C::KSTR + 8 * g];
+    auto kread = [&](int i) {
+      const int mb = i / C::KS, ks = i % C::KS;
+      return *reinterpret_cast<const bf16x8*>(kbase + mb * 32 * C::KSTR +
+                                              16 * ks);
+    };
+    bf16x8 ka[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ka[i] = kread(i);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int mb = i / C::KS, ks = i % C::KS;
+      if (ks == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sn[mb][r] = 0.f;
+      }
+      sn[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i & 3], qf[ks],
+                                                       sn[mb], 0, 0, 0);
+      if (i + 4 < NQK) ka[i & 3] = kread(i + 4);
+      // masked scores are -inf and c > 0, so their weights are exactly 0
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int el = i * EPS + u;
+        const int emb = el >> 4, er = el & 15;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[emb][er], p.c, -mu));
+        sc[emb][er] = e;
+        ls[er & 3] += e;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);  // VALU
+    }
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sc[mb][8 * m + e];
+        pb[mb][m] = __builtin_convertvector(pv, bf16x8);
+      }
+    // O^T += V^T . P^T; V operand reads run two MFMAs ahead.
+    constexpr int NPV = 4 * C::DB;
+    auto vread = [&](int i) {
+      const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
+      return v_operand(buf, mb * 32 + 16 * g + 8 * m, db);
+    };
+    bf16x8 va[3];
+    va[0] = vread(0);
+    va[1] = vread(1);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
+      if (i + 2 < NPV) va[(i + 2) % 3] = vread(i + 2);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[mb][m],
+                                                         oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+  };
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int buf = (t - t0) & 1;
+    // K(t) and V(t-1) are no longer read by anyone: refill their buffers
+    if (t + 2 < t1) dma_k(t + 2, buf);
+    if (t + 1 < t1) dma_v(t + 1, buf ^ 1);
+    if (wave_needs(t)) {
+      tile(t, buf, sc, sn);
+    } else if (t + 1 < t1 && wave_needs(t + 1)) {
+      qk(buf ^ 1, sn);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  // unrolled by two so that the two score buffers swap roles without copies
+  for (int t = t0; t < t1; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < t1) step(t + 1, sb, sa);
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -384,6 +491,10 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   p.window = pr.window;
   p.total = pr.B * pr.Hq * p.nqb;
   p.c = fabsf(pr.scale) * 1.4426950408889634f;
+  // scale 0: every allowed key weighs the same.  A tiny positive factor keeps
+  // masked scores at -inf * c = -inf (weight exactly 0) while every allowed
+  // weight 2^(s*c - m) still rounds to exactly 1.0f, as with c = 0.
+  if (p.c == 0.f) p.c = 1e-30f;
   p.qsign = (pr.scale < 0.f) ? 0x80008000u : 0u;
   if (pr.d == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, dim3(p.total), dim3(kThreads), 0,
