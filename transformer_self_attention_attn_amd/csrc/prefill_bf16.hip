@@ -14,27 +14,32 @@
 // library's own, laid out for CDNA4 wave64 MFMA and LDS.
 //
 // Work decomposition
-//   workgroup = 4 wavefronts = 128 query rows of one head; wave w owns rows
-//   q0 + 32w .. q0 + 32w + 31.  The K/V tile loop walks 64-key tiles that at
-//   least one row of the workgroup may see (tiles entirely above the causal
-//   diagonal, left of the window or past the valid length are never loaded);
-//   a wave skips the arithmetic of tiles that none of its rows may see, and
-//   only tiles that are partly allowed pay for per-element masking.
-//   Query heads of one K/V head are adjacent in the launch order and the
-//   block index is remapped so that each XCD (own L2) works on a contiguous
-//   range of (batch, K/V head) groups; causal blocks run heaviest first.
+//   workgroup = NW wavefronts; wave w owns 32 query rows q0 + 32w .. +31 of
+//   one head.  The K/V tile loop walks 64-key tiles that at least one row of
+//   the workgroup may see (tiles entirely above the causal diagonal, left of
+//   the window or past the valid length are never loaded); a wave skips the
+//   arithmetic of tiles that none of its rows may see, and only tiles that
+//   are partly allowed pay for per-element masking.  Query heads of one K/V
+//   head are adjacent in the launch order and the block index is remapped so
+//   that each XCD (own L2) works on a contiguous range of (batch, K/V head)
+//   groups; causal blocks run heaviest first.
 //
 // Data movement
 //   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
-//   loads (no register staging).  Rows past the valid length are loaded from
-//   a 16-byte block of zeros instead, so padded contents never enter LDS.
-//   LDS rows are padded (K: +16 B, V: +64 B per row); with those strides every
-//   matrix-operand read below touches each LDS bank once, and every operand
-//   address is a per-lane base plus a compile-time offset.  K rows are stored
-//   in the order the 32x32 MFMA wants (see k_row_key); V keeps its natural
-//   [key][d] order and is read with the transposing LDS read
-//   ds_read_b64_tr_b16, which hands each lane four consecutive keys of one
-//   column, exactly the A operand of V^T.
+//   loads (no register staging) into an NS-slot ring.  Rows past the valid
+//   length are loaded from a 16-byte block of zeros instead, so padded
+//   contents never enter LDS.  LDS rows are padded (K: +16 B, V: +64 B per
+//   row); with those strides every matrix-operand read below touches each LDS
+//   bank once, and every operand address is a per-lane base plus a
+//   compile-time offset.  K rows are stored in the order the 32x32 MFMA wants
+//   (see k_row_key); V keeps its natural [key][d] order and is read with the
+//   transposing LDS read ds_read_b64_tr_b16, which hands each lane four
+//   consecutive keys of one column, exactly the A operand of V^T.
+//   Ring slots are compile-time constants in every unrolled step, so the
+//   compiler can tell the slot being filled from the slots being read and
+//   does not stall reads on loads in flight; completion of the tiles needed
+//   next is awaited with an explicit count of outstanding loads, followed by
+//   a plain workgroup barrier.
 //
 // Per tile, per wave (the transposed formulation keeps each query's softmax
 // statistics inside one lane pair):
@@ -47,14 +52,26 @@
 //   O^T[d][query] += V^T . P^T         A = V^T via transposing LDS reads,
 //                                      B = P^T (bf16) taken straight from
 //                                      the S^T accumulator
-// Two-stage software pipeline: while the softmax of tile t runs on the
-// vector ALUs, the S^T product of tile t+1 is already issued to the matrix
-// cores.  K is therefore staged one tile ahead of V; the LDS ring holds
-// K(t+1), K(t+2) and V(t), V(t+1), and the loads of the next tiles are in
-// flight during a whole tile of work.
+// Two-stage software pipeline: the S^T product of tile t+1 is issued to the
+// matrix cores interleaved with the exponentials of tile t, so K runs one
+// tile ahead of V in the ring.
 #include "kernels.h"
 
 #include <cmath>
+#include <type_traits>
+
+// Workgroup shape per head dimension (wavefronts, K/V ring slots), chosen by
+// measurement on MI355X: d=128 runs 8 wavefronts (256 query rows share each
+// K/V tile, one workgroup per CU), d=64 runs 4 (128 rows, two per CU).
+#ifndef MIATTN_PREFILL_NW128
+#define MIATTN_PREFILL_NW128 8
+#endif
+#ifndef MIATTN_PREFILL_NW64
+#define MIATTN_PREFILL_NW64 4
+#endif
+#ifndef MIATTN_PREFILL_NS
+#define MIATTN_PREFILL_NS 2
+#endif
 
 namespace miattn {
 namespace {
@@ -65,33 +82,39 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQW = 32;             // query rows per wavefront
-constexpr int kQB = kQW * kWaves;   // query rows per workgroup
-constexpr int kKT = 64;             // keys per tile
-constexpr float kTau = 8.0f;        // lazy-rescale threshold, log2 units
-constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies
+constexpr int kQW = 32;          // query rows per wavefront
+constexpr int kKT = 64;          // keys per tile
+constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 
 // 16 zero bytes: the source of every direct-to-LDS load of a row past the
 // valid length.
 __device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u,
                                                                      0u};
 
-template <int D>
+template <int D, int NW, int NS>
 struct Cfg {
-  static constexpr int KSTR = D + 8;    // K tile row stride (elements)
-  static constexpr int VSTR = D + 32;   // V tile row stride (elements)
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int QB = kQW * NW;    // query rows per workgroup
+  static constexpr int KSTR = D + 8;     // K tile row stride (elements)
+  static constexpr int VSTR = D + 32;    // V tile row stride (elements)
   static constexpr int KSLOTS = KSTR / 8;  // 16-byte slots per K row
   static constexpr int VSLOTS = VSTR / 8;
   static constexpr int KTILE = kKT * KSTR;
   static constexpr int VTILE = kKT * VSTR;
   static constexpr int KLOADS = kKT * KSLOTS / 64;  // wave-wide 1 KB loads
   static constexpr int VLOADS = kKT * VSLOTS / 64;
+  static constexpr int KLW = (KLOADS + NW - 1) / NW;  // per wave, at most
+  static constexpr int VLW = (VLOADS + NW - 1) / NW;
   static constexpr int KS = D / 16;  // k-steps of the S^T product
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static_assert(kKT * KSLOTS % 64 == 0 && kKT * VSLOTS % 64 == 0, "split");
+  static_assert(KLW + VLW <= 4 * DB, "interleaved loads fit the PV product");
+  static_assert(NS >= 2 && NS <= 4, "ring");
+  static_assert(NS * (KTILE + VTILE) * 2 <= 160 * 1024, "LDS");
 };
 
 // Key held in row r of the K tile in LDS.  Rows are in MFMA row order: with
@@ -103,6 +126,33 @@ __device__ inline int k_row_key(int r) {
   return mb * 32 + ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3);
 }
 
+// Waits until at most n vector-memory loads of this wave are outstanding
+// (the direct-to-LDS loads count there); the other counters are left alone.
+__device__ inline void wait_vmcnt(int n) {
+#define MIATTN_VM(N)                                                      \
+  case N:                                                                 \
+    __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0xF70); \
+    break;
+  switch (n) {
+    MIATTN_VM(0) MIATTN_VM(1) MIATTN_VM(2) MIATTN_VM(3) MIATTN_VM(4)
+    MIATTN_VM(5) MIATTN_VM(6) MIATTN_VM(7) MIATTN_VM(8) MIATTN_VM(9)
+    MIATTN_VM(10) MIATTN_VM(11) MIATTN_VM(12) MIATTN_VM(13) MIATTN_VM(14)
+    MIATTN_VM(15) MIATTN_VM(16) MIATTN_VM(17) MIATTN_VM(18) MIATTN_VM(19)
+    MIATTN_VM(20) MIATTN_VM(21) MIATTN_VM(22) MIATTN_VM(23) MIATTN_VM(24)
+    default:
+      __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  }
+#undef MIATTN_VM
+}
+
+// Workgroup barrier without a memory fence: every LDS read of a tile is
+// consumed within the tile, and the loads the next tile needs were awaited
+// with wait_vmcnt.  The clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ inline void barrier_nofence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
 struct PrefillParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -111,18 +161,40 @@ struct PrefillParams {
   float* lse;
   const int* seqlens;
   int B, Hq, Hkv, N, G, nqb, causal, window, total;
-  float c;         // |scale| * log2(e)
+  float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+template <int I>
+using ic = std::integral_constant<int, I>;
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::VTILE];
+template <int D, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
+  using C = Cfg<D, NW, NS>;
+  // one LDS object per ring slot: the compiler keeps per-object alias
+  // scopes, which lets reads of one slot proceed while another is filled
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[NS > 2 ? C::KTILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks3[NS > 3 ? C::KTILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[C::VTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[C::VTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[NS > 2 ? C::VTILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs3[NS > 3 ? C::VTILE : 8];
+  auto kslot = [&](auto s_c) -> uint16_t* {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (S == 0) return Ks0;
+    else if constexpr (S == 1) return Ks1;
+    else if constexpr (S == 2) return Ks2;
+    else return Ks3;
+  };
+  auto vslot = [&](auto s_c) -> uint16_t* {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (S == 0) return Vs0;
+    else if constexpr (S == 1) return Vs1;
+    else if constexpr (S == 2) return Vs2;
+    else return Vs3;
+  };
 
   // ---- block -> (batch, head, query block) --------------------------------
   const int n = p.total;
@@ -155,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
-  const int q0 = qb * kQB;
+  const int q0 = qb * C::QB;
   const int qw0 = q0 + wave * kQW;
   const int qi = qw0 + ql;
 
@@ -169,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int hi = qlive ? (p.causal ? min(L, qi + 1) : L) : 0;  // exclusive
   const int lo = (qlive && p.window > 0) ? max(0, qi - p.window + 1) : 0;
 
-  const int rows_end = min(q0 + kQB, L);
+  const int rows_end = min(q0 + C::QB, L);
   int t0 = 0, t1 = 0;
   if (rows_end > q0) {
     const int kv_hi = p.causal ? min(L, rows_end) : L;
@@ -208,72 +280,92 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // ---- direct-to-LDS tile loads ---------------------------------------------
   // Wave-wide load i fills LDS bytes [i * 1024, +1024) of the tile: lane l
   // writes 16-byte slot i*64 + l, i.e. (row, chunk) of the padded row.  Loads
-  // are dealt round-robin to the four waves; each lane's source offset within
-  // a tile is fixed, so it is computed once.  Pad chunks are never read and
+  // are dealt round-robin to the waves; each lane's source offset within a
+  // tile is fixed, so it is computed once.  Pad chunks are never read and
   // take the row's first chunk.  Only a tile that runs past the valid length
   // takes the checked path, where such rows read the zero block.
-  constexpr int KLW = (C::KLOADS + kWaves - 1) / kWaves;  // loads per wave
-  constexpr int VLW = (C::VLOADS + kWaves - 1) / kWaves;
-  int koff[KLW], krow_of[KLW], voff[VLW], vrow_of[VLW];
+  unsigned koff[C::KLW], voff[C::VLW];
+  int krow[C::KLW], vrow[C::VLW];
 #pragma unroll
-  for (int n = 0; n < KLW; ++n) {
-    const int slot16 = (wave + kWaves * n) * 64 + lane;
+  for (int m = 0; m < C::KLW; ++m) {
+    const int slot16 = (wave + NW * m) * 64 + lane;
     const int r = slot16 / C::KSLOTS;
     const int c = slot16 - r * C::KSLOTS;
-    krow_of[n] = k_row_key(r);
-    koff[n] = krow_of[n] * D + (c < D / 8 ? c * 8 : 0);
+    krow[m] = k_row_key(r);
+    koff[m] = krow[m] * D + (c < D / 8 ? c * 8 : 0);
   }
 #pragma unroll
-  for (int n = 0; n < VLW; ++n) {
-    const int slot16 = (wave + kWaves * n) * 64 + lane;
+  for (int m = 0; m < C::VLW; ++m) {
+    const int slot16 = (wave + NW * m) * 64 + lane;
     const int r = slot16 / C::VSLOTS;
     const int c = slot16 - r * C::VSLOTS;
-    vrow_of[n] = r;
-    voff[n] = r * D + (c < D / 8 ? c * 8 : 0);
+    vrow[m] = r;
+    voff[m] = r * D + (c < D / 8 ? c * 8 : 0);
   }
-  auto dma = [&](const uint16_t* gsrc, uint16_t* lds, const int (&off)[KLW > VLW ? KLW : VLW],
-                 const int (&row)[KLW > VLW ? KLW : VLW], int nloads, int t) {
+  // Interleaved loads (issued during the PV product): every wave issues
+  // KLW + VLW of them per tile.  A wave without a load number m (uneven
+  // split), and every load of a step whose tiles take the checked path,
+  // reads the zero block into a 1 KB sink: its offset would point past the
+  // tile.
+  __shared__ __attribute__((aligned(16))) uint16_t Sink[512];
+  auto dma_il = [&](const uint16_t* base, uint16_t* slot, bool real,
+                    unsigned off, int i, int nloads) {
+    const bool ok = real && i < nloads;
+    __builtin_amdgcn_global_load_lds(
+        ok ? (const void*)(reinterpret_cast<const char*>(base) + 2u * off)
+           : (const void*)kZero16,
+        (lds_void*)(ok ? slot + i * 512 : Sink), 16, 0, 0);
+  };
+  // loads this wave issues per K tile and per V tile
+  const int kl_w = (C::KLOADS - wave + NW - 1) / NW;
+  const int vl_w = (C::VLOADS - wave + NW - 1) / NW;
+
+  auto dma_k = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
     const int j0 = t * kKT;
-    const uint16_t* base = gsrc + (size_t)j0 * D;
+    const uint16_t* base = kg + (size_t)j0 * D;
     const bool whole = j0 + kKT <= L;
 #pragma unroll
-    for (int n = 0; n < (KLW > VLW ? KLW : VLW); ++n) {
-      const int i = wave + kWaves * n;
-      if (i < nloads) {
-        const void* src = (whole || j0 + row[n] < L)
-                              ? (const void*)(base + off[n])
+    for (int m = 0; m < C::KLW; ++m) {
+      const int i = wave + NW * m;
+      if (i < C::KLOADS) {
+        const void* src = (whole || j0 + krow[m] < L)
+                              ? (const void*)(base + koff[m])
                               : (const void*)kZero16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + i * 512), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(kslot(slot_c) + i * 512),
+                                         16, 0, 0);
       }
     }
   };
-  constexpr int LW = KLW > VLW ? KLW : VLW;
-  int koffw[LW], krw[LW], voffw[LW], vrw[LW];
+  auto dma_v = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    const int j0 = t * kKT;
+    const uint16_t* base = vg + (size_t)j0 * D;
+    const bool whole = j0 + kKT <= L;
 #pragma unroll
-  for (int n = 0; n < LW; ++n) {
-    koffw[n] = n < KLW ? koff[n] : 0;
-    krw[n] = n < KLW ? krow_of[n] : 0;
-    voffw[n] = n < VLW ? voff[n] : 0;
-    vrw[n] = n < VLW ? vrow_of[n] : 0;
-  }
-  auto dma_k = [&](int t, int buf) {
-    dma(kg, Ks[buf], koffw, krw, C::KLOADS, t);
-  };
-  auto dma_v = [&](int t, int buf) {
-    dma(vg, Vs[buf], voffw, vrw, C::VLOADS, t);
+    for (int m = 0; m < C::VLW; ++m) {
+      const int i = wave + NW * m;
+      if (i < C::VLOADS) {
+        const void* src = (whole || j0 + vrow[m] < L)
+                              ? (const void*)(base + voff[m])
+                              : (const void*)kZero16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(vslot(slot_c) + i * 512),
+                                         16, 0, 0);
+      }
+    }
   };
 
-  // ---- S^T = K . Q^T for one tile -----------------------------------------
-  auto qk = [&](int buf, f32x16 (&s)[2]) {
+  // ---- S^T = K . Q^T for one tile (no interleaving) -----------------------
+  auto qk = [&](auto slot_c, f32x16(&s)[2]) {
+    constexpr int S = decltype(slot_c)::value;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const uint16_t* krow = &Ks[buf][(mb * 32 + ql) * C::KSTR + 8 * g];
+      const uint16_t* kr = kslot(slot_c) + (mb * 32 + ql) * C::KSTR + 8 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0,
                                                         0);
       }
@@ -286,20 +378,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int grp16 = lane >> 4;
   const int i16 = lane & 15;
   const int v_lane = (i16 >> 2) * C::VSTR + 16 * (grp16 & 1) + 4 * (i16 & 3);
-  auto v_operand = [&](int buf, int key0, int db) {
-    bf16x8 a;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint16_t* ptr =
-          &Vs[buf][v_lane + (key0 + 4 * half) * C::VSTR + db * 32];
-      const i16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(ptr));
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        a[4 * half + e] = __builtin_bit_cast(__bf16, (short)r4[e]);
-    }
-    return a;
-  };
 
   f32x16 oacc[C::DB];
 #pragma unroll
@@ -309,25 +387,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   float M = -INFINITY;  // running maximum of s * c (log2 units)
   float l = 0.f;        // this lane's half of the running sum
 
-  f32x16 sa[2], sb[2];
-
-  // prologue: K(t0), K(t0+1), V(t0) in LDS; S(t0) in registers
-  if (t1 > t0) {
-    dma_k(t0, 0);
-    dma_v(t0, 0);
-    if (t0 + 1 < t1) dma_k(t0 + 1, 1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t1 > t0 && wave_needs(t0)) qk(0, sa);
-  __syncthreads();
-
-  // One tile of work for a wave, on the scores `sc` of tile t; the S^T
-  // product of tile t+1 is issued into `sn` first, so that its matrix work
-  // overlaps this tile's exponentials (at the end of the range it reads a
-  // stale buffer and the result is dropped).
-  auto tile = [&](int t, int buf, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  float mx_pre = -INFINITY;
+  // One tile of work for a wave, on the scores `sc` of tile t (V slot SV);
+  // the S^T product of tile t+1 (K slot SK) is issued into `sn`, interleaved
+  // with this tile's exponentials (at the end of the range it reads a stale
+  // slot and the result is dropped).
+  // kbi / vbi: tile bases of this step's interleaved K / V loads (into slots
+  // SLK / SLV); real_k / real_v: whether they are this step's real loads.
+  auto tile = [&](auto sv_c, auto sk_c, auto slk_c, auto slv_c,
+                  const uint16_t* kbi, const uint16_t* vbi, bool real_k,
+                  bool real_v, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int SV = decltype(sv_c)::value;
+    constexpr int SK = decltype(sk_c)::value;
     const int j0 = t * kKT;
+    float mx = mx_pre;
     // lane holds keys j0 + mb*32 + g*16 + r (r = 0..15) of query qi
     if (!tile_full(t)) {
 #pragma unroll
@@ -337,12 +410,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           const int j = j0 + mb * 32 + g * 16 + r;
           if (j < lo || j >= hi) sc[mb][r] = -INFINITY;
         }
+      mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float tm = (mx == -INFINITY) ? -INFINITY : mx * p.c;
     const bool need = tm > M + kTau;
@@ -361,9 +434,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 
     // S^T(t+1) = K(t+1) . Q^T interleaved with this tile's exponentials.
     // K operand reads run four MFMAs ahead of their use.
-    constexpr int NQK = 2 * C::KS;       // MFMAs of the S^T product
-    constexpr int EPS = 32 / NQK;        // exponentials per MFMA slot
-    const uint16_t* kbase = &Ks[buf ^ 1][ql * C::KSTR + 8 * g];
+    constexpr int NQK = 2 * C::KS;  // MFMAs of the S^T product
+    constexpr int EPS = 32 / NQK;   // exponentials per MFMA slot
+    const uint16_t* kbase = kslot(sk_c) + ql * C::KSTR + 8 * g;
     auto kread = [&](int i) {
       const int mb = i / C::KS, ks = i % C::KS;
       return *reinterpret_cast<const bf16x8*>(kbase + mb * 32 * C::KSTR +
@@ -392,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         sc[emb][er] = e;
         ls[er & 3] += e;
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);  // VALU
     }
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -411,38 +484,129 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     constexpr int NPV = 4 * C::DB;
     auto vread = [&](int i) {
       const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
-      return v_operand(buf, mb * 32 + 16 * g + 8 * m, db);
+      const int key0 = mb * 32 + 16 * g + 8 * m;
+      bf16x8 a;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint16_t* ptr =
+            vslot(sv_c) + v_lane + (key0 + 4 * half) * C::VSTR + db * 32;
+        const i16x4 r4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a[4 * half + e] = __builtin_bit_cast(__bf16, (short)r4[e]);
+      }
+      return a;
     };
-    bf16x8 va[3];
-    va[0] = vread(0);
-    va[1] = vread(1);
+    float mn2[2] = {-INFINITY, -INFINITY};
+    bf16x8 va[5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) va[i] = vread(i);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
-      if (i + 2 < NPV) va[(i + 2) % 3] = vread(i + 2);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[mb][m],
+      if (i + 4 < NPV) va[(i + 4) % 5] = vread(i + 4);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 5], pb[mb][m],
                                                          oacc[db], 0, 0, 0);
+      mn2[0] = fmaxf(mn2[0], sn[(2 * i) >> 4][(2 * i) & 15]);
+      mn2[1] = fmaxf(mn2[1], sn[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
+      // this step's loads, one per MFMA slot
+      if (i < C::KLW)
+        dma_il(kbi, kslot(slk_c), real_k, koff[i], wave + NW * i, C::KLOADS);
+      else if (i < C::KLW + C::VLW)
+        dma_il(vbi, vslot(slv_c), real_v, voff[i - C::KLW],
+               wave + NW * (i - C::KLW), C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < C::KLW + C::VLW)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
     }
+    mx_pre = fmaxf(mn2[0], mn2[1]);
   };
-  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int buf = (t - t0) & 1;
-    // K(t) and V(t-1) are no longer read by anyone: refill their buffers
-    if (t + 2 < t1) dma_k(t + 2, buf);
-    if (t + 1 < t1) dma_v(t + 1, buf ^ 1);
-    if (wave_needs(t)) {
-      tile(t, buf, sc, sn);
+
+  f32x16 sa[2], sb[2];
+
+  // ---- prologue: K(t0 .. t0+NS-1) and V(t0 .. t0+NS-2) in flight ----------
+  if (t1 > t0) {
+    dma_k(ic<0>(), t0);
+    dma_v(ic<0>(), t0);
+    if (t0 + 1 < t1) dma_k(ic<1>(), t0 + 1);
+    if constexpr (NS >= 3) {
+      if (t0 + 1 < t1) dma_v(ic<1>(), t0 + 1);
+      if (t0 + 2 < t1) dma_k(ic<2 % NS>(), t0 + 2);
+    }
+    if constexpr (NS >= 4) {
+      if (t0 + 2 < t1) dma_v(ic<2>(), t0 + 2);
+      if (t0 + 3 < t1) dma_k(ic<3 % NS>(), t0 + 3);
+    }
+  }
+  wait_vmcnt(0);
+  barrier_nofence();
+  if (t1 > t0 && wave_needs(t0)) {
+    qk(ic<0>(), sa);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx_pre = fmaxf(mx_pre, sa[mb][r]);
+  }
+  barrier_nofence();
+
+  // Loads this wave issues in the iteration for tile t.
+  auto issued = [&](int t) {
+    return (t + NS - 1 < t1 ? vl_w : 0) + (t + NS < t1 ? kl_w : 0);
+  };
+  // Iteration for tile t = t0 + k, with k % NS == KK: V(t) is in slot KK and
+  // K(t+1) in slot (KK+1) % NS.  It refills V(t+NS-1) into slot
+  // (KK+NS-1) % NS (held V(t-1), done) and K(t+NS) into slot KK (held K(t),
+  // done).
+  auto step = [&](auto kk_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int KK = decltype(kk_c)::value;
+    constexpr int SLV = (KK + NS - 1) % NS;
+    const int tk = t + NS;      // K tile for slot KK
+    const int tv = t + NS - 1;  // V tile for slot SLV
+    const bool whole_k = tk < t1 && (tk + 1) * kKT <= L;
+    const bool whole_v = tv < t1 && (tv + 1) * kKT <= L;
+    const bool il = wave_needs(t);  // this wave's loads go inside its tile
+    if (!(il && whole_v) && tv < t1) dma_v(ic<SLV>(), tv);
+    if (!(il && whole_k) && tk < t1) dma_k(ic<KK>(), tk);
+    if (il) {
+      // (a base is only dereferenced when its tile is whole)
+      tile(ic<KK>(), ic<(KK + 1) % NS>(), ic<KK>(), ic<SLV>(),
+           kg + (size_t)(whole_k ? tk : 0) * kKT * D,
+           vg + (size_t)(whole_v ? tv : 0) * kKT * D, whole_k, whole_v, t,
+           sc, sn);
     } else if (t + 1 < t1 && wave_needs(t + 1)) {
-      qk(buf ^ 1, sn);
+      qk(ic<(KK + 1) % NS>(), sn);
+      mx_pre = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx_pre = fmaxf(mx_pre, sn[mb][r]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // K(t+2) and V(t+1) were issued in the iteration for tile t+2-NS (or in
+    // the prologue); only the loads of later iterations may stay in flight.
+    int later = 0;
+#pragma unroll
+    for (int d = 0; d < NS - 2; ++d)
+      if (t - d >= t0) later += issued(t - d);
+    wait_vmcnt(later);
+    barrier_nofence();
   };
-  // unrolled by two so that the two score buffers swap roles without copies
-  for (int t = t0; t < t1; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < t1) step(t + 1, sb, sa);
+  // Unrolled by 2*NS: every ring slot index is a compile-time constant and
+  // the two score buffers swap roles without copies.
+  for (int t = t0; t < t1; t += 2 * NS) {
+    step(ic<0>(), t, sa, sb);
+    if (t + 1 < t1) step(ic<1 % NS>(), t + 1, sb, sa);
+    if (t + 2 < t1) step(ic<2 % NS>(), t + 2, sa, sb);
+    if (t + 3 < t1) step(ic<3 % NS>(), t + 3, sb, sa);
+    if constexpr (NS >= 3) {
+      if (t + 4 < t1) step(ic<4 % NS>(), t + 4, sa, sb);
+      if (t + 5 < t1) step(ic<5 % NS>(), t + 5, sb, sa);
+    }
+    if constexpr (NS >= 4) {
+      if (t + 6 < t1) step(ic<6 % NS>(), t + 6, sa, sb);
+      if (t + 7 < t1) step(ic<7 % NS>(), t + 7, sb, sa);
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -469,6 +633,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   }
 }
 
+template <int D, int NW, int NS>
+void launch(const PrefillParams& p0, hipStream_t stream) {
+  using C = Cfg<D, NW, NS>;
+  PrefillParams p = p0;
+  p.nqb = (p.N + C::QB - 1) / C::QB;
+  p.total = p.B * p.Hq * p.nqb;
+  hipLaunchKernelGGL((prefill_kernel<D, NW, NS>), dim3(p.total),
+                     dim3(C::THREADS), 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
@@ -486,10 +660,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   p.Hkv = pr.Hkv;
   p.N = pr.Nq;
   p.G = pr.Hq / pr.Hkv;
-  p.nqb = (pr.Nq + kQB - 1) / kQB;
   p.causal = pr.causal;
   p.window = pr.window;
-  p.total = pr.B * pr.Hq * p.nqb;
   p.c = fabsf(pr.scale) * 1.4426950408889634f;
   // scale 0: every allowed key weighs the same.  A tiny positive factor keeps
   // masked scores at -inf * c = -inf (weight exactly 0) while every allowed
@@ -497,11 +669,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   if (p.c == 0.f) p.c = 1e-30f;
   p.qsign = (pr.scale < 0.f) ? 0x80008000u : 0u;
   if (pr.d == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(p.total), dim3(kThreads), 0,
-                       stream, p);
+    launch<128, MIATTN_PREFILL_NW128, MIATTN_PREFILL_NS>(p, stream);
   else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(p.total), dim3(kThreads), 0,
-                       stream, p);
+    launch<64, MIATTN_PREFILL_NW64, MIATTN_PREFILL_NS>(p, stream);
   return hipGetLastError();
 }
 
