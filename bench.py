@@ -12,8 +12,18 @@ kernels run on.  The fp64 CPU oracle is timed on a bounded sample of the
 prefill workload as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--copy-probe MIB]
+       python bench.py --fold-traffic FETCH.csv WRITE.csv
 Prints one JSON line.
+
+HBM traffic: two rocprofv3 counter runs of a short bench with
+`--copy-probe 1024` (one with `--pmc FETCH_SIZE`, one with
+`--pmc WRITE_SIZE`, each with `--output-format csv`) record the counters for
+the attention kernels and for a plain device-to-device copy of known size;
+`--fold-traffic` scales each kernel's counters by what the copy read and wrote
+per byte and stores bytes per launch, with the kernel sources' hashes, in
+profiles/traffic.json.  bench.py reports them only while the sources are
+unchanged.
 """
 
 import argparse
@@ -92,6 +102,63 @@ def traffic_for(kind):
     return rec.get("hbm_bytes_per_launch")
 
 
+TRAFFIC_KERNELS = {
+    "prefill": ("prefill_kernel",),
+    "decode": ("decode_split_kernel", "decode_combine_kernel"),
+}
+COPY_KERNEL = "copyBuffer"
+
+
+def read_counter_csv(path, counter):
+    """{dispatch_id: (kernel_name, value)} for one counter of a rocprofv3
+    counter_collection.csv (values summed over the rows of a dispatch)."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            d = int(row["Dispatch_Id"])
+            name, v = out.get(d, (row["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(row["Counter_Value"]))
+    return out
+
+
+def fold_traffic(fetch_csv, write_csv, copy_bytes):
+    """Per-launch HBM bytes of the attention kernels from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by copy_bytes over what the
+    same counter read for the probe copy of copy_bytes bytes."""
+    rec = {}
+    scale = {}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = read_counter_csv(path, counter)
+        probe = [v for n, v in disp.values()
+                 if COPY_KERNEL in n and 0.5 < v * 1024 / copy_bytes < 2.0]
+        if not probe:
+            raise SystemExit(f"no probe copy of ~{copy_bytes} B in {path}")
+        kib = sorted(probe)[len(probe) // 2]
+        scale[counter] = copy_bytes / (kib * 1024.0)
+        per[counter] = disp
+    for kind, names in TRAFFIC_KERNELS.items():
+        total = 0.0
+        parts = {}
+        for nm in names:
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                vals = sorted(v for n, v in per[counter].values() if nm in n)
+                if not vals:
+                    raise SystemExit(f"{nm} not found for {counter}")
+                b = vals[len(vals) // 2] * 1024.0 * scale[counter]
+                parts[f"{nm}:{counter}"] = b
+                total += b
+        rec[kind] = {"hbm_bytes_per_launch": total, "parts": parts,
+                     "source_sha256": source_sha(KERNEL_SOURCES[kind])}
+    rec["copy_probe"] = {"bytes": copy_bytes,
+                         "scale_fetch": scale["FETCH_SIZE"],
+                         "scale_write": scale["WRITE_SIZE"]}
+    return rec
+
+
 def cpu_baseline(w, x, budget_s=20.0):
     """Times the fp64 oracle (as it stands) on whole (batch, head) slices of
     the prefill workload, in order, until about `budget_s` seconds of CPU
@@ -134,7 +201,20 @@ def main():
     ap.add_argument("--reps", type=int, default=200,
                     help="repetitions of the trimmed-mean latency protocol")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy MIB MiB device to "
+                         "device three times (counter calibration)")
+    ap.add_argument("--fold-traffic", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="fold two counter CSVs into profiles/traffic.json")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the probe copy the CSVs hold")
     args = ap.parse_args()
+    if args.fold_traffic:
+        rec = fold_traffic(*args.fold_traffic, args.copy_mib << 20)
+        with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus "
               f"{args.gpus}); this build has no multi-GPU path.",
@@ -237,6 +317,15 @@ def main():
     proto_p = reps(lambda i: prefill())
     proto_d = reps(decode)
 
+    if args.copy_probe:
+        n = (args.copy_probe << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -267,7 +356,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for("prefill"),
-            "kernel": "prefill_kernel<128>",
+            "kernel": "prefill_kernel<128, 8, 2>",
             "algorithmic_flop_per_launch": flops,
             "avg_launch_ms": round(pre_avg, 5),
         },
@@ -281,7 +370,7 @@ def main():
                 "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for("decode"),
-                "kernels": "decode_split_kernel<128,4> + "
+                "kernels": "decode_split_kernel<128, 4> + "
                            "decode_combine_kernel<128>",
                 "algorithmic_bytes_per_launch": dbytes,
                 "avg_launch_ms": round(dec_avg, 5),
