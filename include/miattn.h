@@ -64,7 +64,9 @@ enum miattn_status {
   MIATTN_OK = 0,
   MIATTN_ERR_INVALID = -1,      /* null pointer, size <= 0, Hq % Hkv != 0,
                                    Nq > Nk, window < 0, non-finite scale,
-                                   pointer not 16-byte aligned, size overflow */
+                                   pointer not 16-byte aligned, size overflow,
+                                   bf16 decode (Nq == 1) with
+                                   Nk > 33553920 */
   MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; window > 0 without
                                    causal; Nq not in {1, Nk} */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */

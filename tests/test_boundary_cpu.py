@@ -64,7 +64,6 @@ BAD = [
     (dict(d=256), mi.MIATTN_ERR_UNSUPPORTED, "head dim"),
     (dict(window=8, causal=0), mi.MIATTN_ERR_UNSUPPORTED, "causal"),
     (dict(Nq=32), mi.MIATTN_ERR_UNSUPPORTED, "decode"),
-    (dict(B=70000, Nq=1), mi.MIATTN_ERR_INVALID, "65535"),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 12, Nk=1 << 12),
      mi.MIATTN_ERR_INVALID, "too large"),
 ]
@@ -79,6 +78,14 @@ def test_rejected_on_host(fn_name, over, code, msg):
     assert rc == code
     err = mi.attn_last_error()
     assert fn_name in err and msg in err, err
+
+
+def test_decode_key_limit_on_host():
+    # the bf16 decode grid covers at most 65535 splits of 512 keys; longer
+    # caches are refused before any HIP call
+    rc = call(mi.attn_fwd, good(Nq=1, Nk=65535 * 512 + 1))
+    assert rc == mi.MIATTN_ERR_INVALID
+    assert "at most 33553920" in mi.attn_last_error()
 
 
 def test_lse_may_be_null_and_still_validated():

@@ -61,15 +61,13 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
     return fail(MIATTN_ERR_UNSUPPORTED,
                 "%s: Nq=%d must be 1 (decode) or Nk=%d (prefill)", fn, Nq, Nk);
   // index arithmetic bounds: element offsets are 64-bit, row and block
-  // counts are 32-bit, decode grid y/z are limited to 65535
+  // counts are 32-bit
   const long long qrows = (long long)B * Hq * Nq;
   const long long qblocks = (long long)B * Hq * ((Nq + 127) / 128);
   if (qrows > 0x7fffffffLL || qblocks > 0x7fffffffLL ||
       (long long)B * Hkv * Nk > 0x7fffffffLL)
     return fail(MIATTN_ERR_INVALID, "%s: problem too large for one launch",
                 fn);
-  if (Nq == 1 && (B > 65535 || Hq > 65535))
-    return fail(MIATTN_ERR_INVALID, "%s: decode needs B and Hq <= 65535", fn);
   return MIATTN_OK;
 }
 
@@ -140,6 +138,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (Nq == 1) {
+    if (Nk > miattn::decode_max_keys())
+      return fail(MIATTN_ERR_INVALID,
+                  "attn_fwd: decode supports at most %d cache rows (Nk=%d)",
+                  miattn::decode_max_keys(), Nk);
     void* ws = nullptr;
     rc = workspace(miattn::decode_workspace_bytes(p), &ws);
     if (rc != MIATTN_OK) return rc;

@@ -9,16 +9,22 @@
 // Pass 1 (decode_split_kernel): grid = splits x (K/V head, head chunk) x batch.
 //   A workgroup owns a chunk of kChunk keys of one (batch, K/V head) and the
 //   GB query heads of that group that share it, so each K and V byte is read
-//   from HBM exactly once for all of them.
-//     K sweep: s_hj = scale * q_h . k_j for the chunk (dot products of bf16
-//              pairs in fp32, reduced across the lanes that share a key row
-//              with DPP), kept in LDS in log2 units;
-//     softmax: per head, m_h = max_j s_hj and l_h = sum_j 2^(s_hj - m_h) over
-//              the chunk (workgroup reductions);
-//     V sweep: o_h = sum_j 2^(s_hj - m_h) v_j / l_h.
-//   It writes the chunk's partial result o_s (fp32) and lse_s = (m + log2 l)
-//   ln 2 to the workspace.  Chunks that hold no allowed key exit at once.
-// Pass 2 (decode_combine_kernel): grid = query heads x batch.
+//   from HBM exactly once for all of them.  The chunk is one pass over its
+//   key rows: every group of D/8 lanes takes every (kThreads*8/D)-th row,
+//   loads its K and V together (16 B per lane each, non-temporal: the cache
+//   is streamed once) and keeps, per head, an online softmax of its own rows:
+//     s = scale * q . k       (bf16 pair dot products in fp32, summed across
+//                              the group's lanes with DPP), in log2 units;
+//     m = running maximum, moved (and l, o rescaled) only when a score
+//         exceeds it by more than 2^8;
+//     l += 2^(s - m);  o += 2^(s - m) v.
+//   A register ring keeps the next kRing-1 batches of rows in flight, and
+//   nothing waits on other lanes until the chunk ends.  Then the groups are
+//   merged (shifts to a common maximum) across lanes and, through LDS,
+//   across the wavefronts.  The workgroup writes the chunk's partial result
+//   o_s = o / l (fp32) and lse_s = (m + log2 l) ln 2 to the workspace.
+//   Chunks that hold no allowed key exit at once.
+// Pass 2 (decode_combine_kernel): one wavefront per (batch, query head).
 //   lse = log sum_s exp(lse_s) (max-shifted) and o = sum_s exp(lse_s - lse) o_s,
 //   the softmax definition applied to a partition of the keys; written as bf16
 //   o and fp32 lse.
@@ -32,10 +38,22 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+#ifndef MIATTN_DECODE_EAGER
+#define MIATTN_DECODE_EAGER 0
+#endif
+#ifndef MIATTN_DECODE_RING
+#define MIATTN_DECODE_RING 4
+#endif
+
 constexpr int kThreads = 256;
-constexpr int kChunk = 512;  // keys per split
-constexpr int kUnroll = 4;   // key rows in flight per lane
+#ifndef MIATTN_DECODE_CHUNK
+#define MIATTN_DECODE_CHUNK 512
+#endif
+constexpr int kChunk = MIATTN_DECODE_CHUNK;  // keys per split
+constexpr int kRing = MIATTN_DECODE_RING;  // key-row batches per lane in flight + 1
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 constexpr int kMaxGB = 8;    // query heads per workgroup
+constexpr int kCombineWaves = 4;  // (batch, head) rows per combine workgroup
 
 struct DecodeParams {
   const uint16_t* q;
@@ -90,6 +108,12 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
+// K and V rows are read once per call: streaming (non-temporal) loads keep
+// them from displacing reusable lines in the caches.
+__device__ inline u32x4 load_stream(const uint16_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+}
+
 __device__ inline float bf16_lo(unsigned w) {
   return __builtin_bit_cast(float, w << 16);
 }
@@ -100,34 +124,32 @@ __device__ inline float bf16_hi(unsigned w) {
 template <int D, int GB>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     DecodeParams p) {
-  constexpr int LPK = D / 8;             // lanes per key row (16 B each)
-  constexpr int KPI = kThreads / LPK;    // key rows per workgroup step
-  constexpr int STEPS = kChunk / KPI;
-  static_assert(STEPS % kUnroll == 0, "chunk split");
-  __shared__ float sc[kChunk * GB];           // scores, then weights
-  __shared__ float red[kThreads / 64][GB];    // cross-wave reductions
-  __shared__ float ored[kThreads / 64][GB * D];
+  constexpr int LPK = D / 8;           // lanes per key row (16 B each)
+  constexpr int GPW = 64 / LPK;        // row groups per wavefront
+  constexpr int NWV = kThreads / 64;   // wavefronts per workgroup
+  constexpr int RPB = kThreads / LPK;  // key rows per batch (one per group)
+  constexpr int R = kRing;             // batches held in registers
+  __shared__ float red_o[NWV][GB * D];
+  __shared__ float red_ml[NWV][2 * GB];
 
-  const int s = blockIdx.x;
-  const int hk = blockIdx.y / p.nhc;
-  const int hc = blockIdx.y - hk * p.nhc;
-  const int b = blockIdx.z;
-  int lo, L;
-  key_range(p, b, lo, L);
-  const int c0 = s * kChunk;
-  const int c1 = min(c0 + kChunk, L);
-  const int a0 = max(c0, lo);
-  if (a0 >= c1) return;  // no allowed key here; the combine skips this split
-
+  // grid x = (batch, K/V head, head chunk), fastest; grid y = split.
+  // Workgroups are dealt to the XCDs round-robin in launch order, so each
+  // XCD sees every split index equally often, whatever the valid lengths.
+  const int s = blockIdx.y;
+  const int nx = p.Hkv * p.nhc;
+  const int b = blockIdx.x / nx;
+  const int hk = (blockIdx.x - b * nx) / p.nhc;
+  const int hc = blockIdx.x - b * nx - hk * p.nhc;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int dch = tid % LPK;  // 8-column chunk of the row this lane reads
-  const int krow = tid / LPK;
+  const int grp = tid / LPK;  // row group: rows c0 + i * RPB + grp
   const int h0 = hk * p.G + hc * GB;
   const int nh = min(GB, p.G - hc * GB);
 
-  // query fragments: 8 columns of each head, as bf16 pairs
+  // query fragments (8 columns of each head as bf16 pairs); issued before
+  // the valid length is known, the address does not depend on it
   unsigned qw[GB][4];
 #pragma unroll
   for (int gi = 0; gi < GB; ++gi) {
@@ -139,175 +161,201 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int e = 0; e < 4; ++e) qw[gi][e] = raw[e];
   }
 
+  int lo, L;
+  key_range(p, b, lo, L);
+  const int c0 = s * kChunk;
+  const int c1 = min(c0 + kChunk, L);
+  const int a0 = max(c0, lo);
+  if (a0 >= c1) return;  // no allowed key here; the combine skips this split
+  const int first = (a0 - c0) / RPB;
+  const int nb = (c1 - c0 + RPB - 1) / RPB;  // batches first .. nb-1
+
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
   const uint16_t* kg = p.k + kv_base + dch * 8;
   const uint16_t* vg = p.v + kv_base + dch * 8;
 
-  // ---- K sweep: scores --------------------------------------------------
-  for (int it = 0; it < STEPS; it += kUnroll) {
-    u32x4 kk[kUnroll];
+  // ring of R batches: batch i sits in slot (i - first) % R.  Every lane
+  // loads on every step (no branch around the loads, so the hardware's
+  // in-order load counter tells exactly when a slot has arrived); a row
+  // outside [a0, c1) is clamped to an allowed row, read again from cache,
+  // and masked out of the softmax.
+  u32x4 kr[R], vr[R];
+  auto issue = [&](int i, u32x4& kd, u32x4& vd) {
+    const int key = min(max(c0 + i * RPB + grp, a0), c1 - 1);
+    kd = load_stream(kg + (size_t)key * D);
+    vd = load_stream(vg + (size_t)key * D);
+  };
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int key = c0 + (it + u) * KPI + krow;
-      kk[u] = (key >= a0 && key < c1)
-                  ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * D)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int key = c0 + (it + u) * KPI + krow;
-      const bool ok = key >= a0 && key < c1;
-#pragma unroll
-      for (int gi = 0; gi < GB; ++gi) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // copy the vector element out first: bit-casting the element
-          // expression itself would read element 0
-          const unsigned kw = kk[u][e];
-          const unsigned qv = qw[gi][e];
-          acc = __builtin_amdgcn_fdot2_f32_bf16(
-              __builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qv),
-              acc, false);
-        }
-        acc = group_sum<LPK>(acc);
-        if (dch == 0)
-          sc[(key - c0) * GB + gi] = ok ? acc * p.c : -INFINITY;
-      }
-    }
-  }
-  __syncthreads();
+  for (int r = 0; r < R - 1; ++r) issue(first + r, kr[r], vr[r]);
 
-  // ---- chunk softmax statistics per head -------------------------------
-  float mh[GB], lh[GB];
+  // per row group and head: running max m (log2 units), sum l, output o
+  float m[GB], l[GB], o[GB][8];
 #pragma unroll
   for (int gi = 0; gi < GB; ++gi) {
-    float m = -INFINITY;
-    for (int j = tid; j < kChunk; j += kThreads) m = fmaxf(m, sc[j * GB + gi]);
-    m = wave_max(m);
-    if (lane == 0) red[wave][gi] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
-    float m = red[0][gi];
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w][gi]);
-    mh[gi] = m;  // finite: the chunk holds at least one allowed key
-  }
-  __syncthreads();
-#pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
-    float sum = 0.f;
-    for (int j = tid; j < kChunk; j += kThreads) {
-      const float e = __builtin_amdgcn_exp2f(sc[j * GB + gi] - mh[gi]);
-      sc[j * GB + gi] = e;
-      sum += e;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) red[wave][gi] = sum;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
-    float sum = 0.f;
-    for (int w = 0; w < kThreads / 64; ++w) sum += red[w][gi];
-    lh[gi] = sum;
-  }
-
-  // ---- V sweep: weighted sum -------------------------------------------
-  float o[GB][8];
-#pragma unroll
-  for (int gi = 0; gi < GB; ++gi)
+    m[gi] = -INFINITY;
+    l[gi] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[gi][e] = 0.f;
-  for (int it = 0; it < STEPS; it += kUnroll) {
-    u32x4 vv[kUnroll];
+  }
+
+  // whole rounds of R steps; steps past the last batch are fully masked
+  for (int i0 = first; i0 < nb; i0 += R) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int key = c0 + (it + u) * KPI + krow;
-      vv[u] = (key >= a0 && key < c1)
-                  ? *reinterpret_cast<const u32x4*>(vg + (size_t)key * D)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int r = 0; r < R; ++r) {
+      const int i = i0 + r;
+      {
+        // keep R - 1 batches in flight: refill the slot freed last step
+        issue(i + R - 1, kr[(r + R - 1) % R], vr[(r + R - 1) % R]);
+        const int key = c0 + i * RPB + grp;
+        const bool ok = key >= a0 && key < c1;
+        float sc[GB];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int jl = (it + u) * KPI + krow;  // key - c0
-      float x[8];
+        for (int gi = 0; gi < GB; ++gi) {
+          float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_lo(vv[u][e]);
-        x[2 * e + 1] = bf16_hi(vv[u][e]);
-      }
+          for (int e = 0; e < 4; ++e) {
+            const unsigned kw = kr[r][e];
+            const unsigned qv = qw[gi][e];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qv),
+                acc, false);
+          }
+          acc = group_sum<LPK>(acc);
+          sc[gi] = ok ? acc * p.c : -INFINITY;
+        }
+        // move the running maximum only when a score exceeds it by more
+        // than 2^tau (any common shift of a row's scores is exact)
+#if MIATTN_DECODE_EAGER
+        {
+#else
+        bool grow = false;
 #pragma unroll
-      for (int gi = 0; gi < GB; ++gi) {
-        const float w = sc[jl * GB + gi];  // 0 for keys that are not allowed
+        for (int gi = 0; gi < GB; ++gi) grow |= sc[gi] > m[gi] + kTau;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#endif
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[gi][e] = fmaf(w, x[e], o[gi][e]);
+          for (int gi = 0; gi < GB; ++gi) {
+            const float mn = fmaxf(m[gi], sc[gi]);
+            const float a =
+                mn == m[gi] ? 1.0f : __builtin_amdgcn_exp2f(m[gi] - mn);
+            m[gi] = mn;
+            l[gi] *= a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[gi][e] *= a;
+          }
+        }
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned vw = vr[r][e];
+          x[2 * e] = bf16_lo(vw);
+          x[2 * e + 1] = bf16_hi(vw);
+        }
+#pragma unroll
+        for (int gi = 0; gi < GB; ++gi) {
+          const float pw = ok ? __builtin_amdgcn_exp2f(sc[gi] - m[gi]) : 0.f;
+          l[gi] += pw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[gi][e] = fmaf(pw, x[e], o[gi][e]);
+        }
       }
     }
   }
-  // lanes with the same column chunk hold different keys: add them up
+
+  // merge the row groups: first the GPW groups of each wavefront (lanes
+  // that differ in the row-group bits), then the wavefronts through LDS
 #pragma unroll
-  for (int gi = 0; gi < GB; ++gi)
+  for (int gi = 0; gi < GB; ++gi) {
+    float mw = m[gi];
+    for (int x = LPK; x < 64; x <<= 1) mw = fmaxf(mw, __shfl_xor(mw, x));
+    const float a =
+        m[gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gi] - mw);
+    float lw = l[gi] * a;
+    for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = o[gi][e];
-      for (int m = LPK; m < 64; m <<= 1) x += __shfl_xor(x, m);
-      o[gi][e] = x;
+      float y = o[gi][e] * a;
+      for (int x = LPK; x < 64; x <<= 1) y += __shfl_xor(y, x);
+      o[gi][e] = y;
     }
+    m[gi] = mw;
+    l[gi] = lw;
+  }
   if (lane < LPK) {
 #pragma unroll
     for (int gi = 0; gi < GB; ++gi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ored[wave][gi * D + dch * 8 + e] = o[gi][e];
+      for (int e = 0; e < 8; ++e) red_o[wave][gi * D + dch * 8 + e] = o[gi][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi) {
+      red_ml[wave][gi] = m[gi];
+      red_ml[wave][GB + gi] = l[gi];
+    }
   }
   __syncthreads();
   for (int t = tid; t < nh * D; t += kThreads) {
     const int gi = t / D;
     const int d = t - gi * D;
-    float x = 0.f;
-    for (int w = 0; w < kThreads / 64; ++w) x += ored[w][t];
-    float lsum = 0.f, mval = 0.f;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int g2 = 0; g2 < GB; ++g2)
-      if (g2 == gi) {
-        lsum = lh[g2];
-        mval = mh[g2];
-      }
+    for (int w = 0; w < NWV; ++w) mx = fmaxf(mx, red_ml[w][gi]);
+    float x = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = red_ml[w][gi];
+      const float a = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
+      x = fmaf(a, red_o[w][t], x);
+      lsum = fmaf(a, red_ml[w][GB + gi], lsum);
+    }
     const size_t row = (size_t)(b * p.Hq + h0 + gi) * p.nsplit + s;
     p.ws_o[row * D + d] = x / lsum;
-    if (d == 0)
-      p.ws_lse[row] = (mval + log2f(lsum)) * 0.69314718055994531f;
+    if (d == 0) p.ws_lse[row] = (mx + log2f(lsum)) * 0.69314718055994531f;
   }
 }
 
+// One wavefront per (batch, query head); lane l owns columns l*CPL..+CPL-1.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
+    DecodeParams p) {
+  constexpr int CPL = D / 64;
+  const int r = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (r >= p.B * p.Hq) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int b = r / p.Hq;
   int lo, L;
   key_range(p, b, lo, L);
-  const size_t row0 = (size_t)(b * p.Hq + h) * p.nsplit;
-  uint16_t* orow = p.o + (size_t)(b * p.Hq + h) * D;
+  const size_t row0 = (size_t)r * p.nsplit;
+  uint16_t* orow = p.o + (size_t)r * D + lane * CPL;
   if (L <= lo) {  // no allowed key
-    orow[d] = 0;
-    if (d == 0 && p.lse) p.lse[b * p.Hq + h] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) orow[e] = 0;
+    if (lane == 0 && p.lse) p.lse[r] = -INFINITY;
     return;
   }
   const int s0 = lo / kChunk;
   const int s1 = (L + kChunk - 1) / kChunk;
   float m = -INFINITY;
-  for (int s = s0; s < s1; ++s) m = fmaxf(m, p.ws_lse[row0 + s]);
-  float wsum = 0.f, acc = 0.f;
+  for (int s = s0 + lane; s < s1; s += 64) m = fmaxf(m, p.ws_lse[row0 + s]);
+  m = wave_max(m);
+  float acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+#pragma unroll 4
   for (int s = s0; s < s1; ++s) {
     const float w = expf(p.ws_lse[row0 + s] - m);
     wsum += w;
-    acc = fmaf(w, p.ws_o[(row0 + s) * D + d], acc);
+    const float* src = p.ws_o + (row0 + s) * D + lane * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] = fmaf(w, src[e], acc[e]);
   }
-  const __bf16 ob = (__bf16)(acc / wsum);
-  orow[d] = __builtin_bit_cast(uint16_t, ob);
-  if (d == 0 && p.lse) p.lse[b * p.Hq + h] = m + logf(wsum);
+  const float inv = 1.0f / wsum;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e)
+    orow[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[e] * inv));
+  if (lane == 0 && p.lse) p.lse[r] = m + logf(wsum);
 }
 
 int heads_per_block(int G) {
@@ -320,7 +368,7 @@ int heads_per_block(int G) {
 template <int D, int GB>
 void launch_split(const DecodeParams& p, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<D, GB>),
-                     dim3(p.nsplit, p.Hkv * p.nhc, p.B), dim3(kThreads), 0, st,
+                     dim3(p.B * p.Hkv * p.nhc, p.nsplit), dim3(kThreads), 0, st,
                      p);
 }
 
@@ -339,6 +387,8 @@ void launch_split_d(const DecodeParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+int decode_max_keys() { return 65535 * kChunk; }
 
 size_t decode_workspace_bytes(const Problem& pr) {
   const size_t nsplit = (size_t)((pr.Nk + kChunk - 1) / kChunk);
@@ -369,14 +419,15 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   const size_t rows = (size_t)pr.B * pr.Hq * p.nsplit;
   p.ws_o = static_cast<float*>(ws);
   p.ws_lse = p.ws_o + rows * pr.d;
+  const int ncomb = (pr.B * pr.Hq + kCombineWaves - 1) / kCombineWaves;
   if (pr.d == 128) {
     launch_split_d<128>(p, stream);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(pr.Hq, pr.B),
-                       dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(ncomb),
+                       dim3(64 * kCombineWaves), 0, stream, p);
   } else {
     launch_split_d<64>(p, stream);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(pr.Hq, pr.B), dim3(64),
-                       0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(ncomb),
+                       dim3(64 * kCombineWaves), 0, stream, p);
   }
   return hipGetLastError();
 }
