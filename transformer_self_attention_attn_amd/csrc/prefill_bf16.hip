@@ -223,7 +223,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // Nq == Nk: the first L rows are live and row i sits at position i.
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar: load numbers and LDS destinations derived from
+  // it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
@@ -445,6 +447,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     bf16x8 ka[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ka[i] = kread(i);
+    // keep the first operand reads ahead of the interleaved loop: the
+    // scheduler fills the loop's LDS-read slots in program order
+    __builtin_amdgcn_sched_barrier(0);
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
@@ -502,6 +507,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     bf16x8 va[5];
 #pragma unroll
     for (int i = 0; i < 4; ++i) va[i] = vread(i);
+    // keep the first operand reads ahead of the interleaved loop: the
+    // scheduler fills the loop's LDS-read slots in program order
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
