@@ -356,7 +356,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for("prefill"),
-            "kernel": "prefill_kernel<128, 8, 2>",
+            "kernel": "prefill_kernel<128, 8>",
             "algorithmic_flop_per_launch": flops,
             "avg_launch_ms": round(pre_avg, 5),
         },

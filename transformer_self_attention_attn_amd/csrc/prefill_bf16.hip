@@ -26,7 +26,8 @@
 //
 // Data movement
 //   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
-//   loads (no register staging) into an NS-slot ring.  Rows past the valid
+//   loads (no register staging) into rings of two K and three V slots, each
+//   wave issuing its share of a tile's loads.  Rows past the valid
 //   length are loaded from a 16-byte block of zeros instead, so padded
 //   contents never enter LDS.  LDS rows are padded (K: +16 B, V: +64 B per
 //   row); with those strides every matrix-operand read below touches each LDS
@@ -38,8 +39,8 @@
 //   Ring slots are compile-time constants in every unrolled step, so the
 //   compiler can tell the slot being filled from the slots being read and
 //   does not stall reads on loads in flight; completion of the tiles needed
-//   next is awaited with an explicit count of outstanding loads, followed by
-//   a plain workgroup barrier.
+//   next is awaited with an explicit wait on outstanding loads, followed by a
+//   plain workgroup barrier.
 //
 // Per tile, per wave (the transposed formulation keeps each query's softmax
 // statistics inside one lane pair):
@@ -52,25 +53,25 @@
 //   O^T[d][query] += V^T . P^T         A = V^T via transposing LDS reads,
 //                                      B = P^T (bf16) taken straight from
 //                                      the S^T accumulator
-// Two-stage software pipeline: the S^T product of tile t+1 is issued to the
-// matrix cores interleaved with the exponentials of tile t, so K runs one
-// tile ahead of V in the ring.
+// Two-stage software pipeline: X(t) issues the S^T product of tile t+1 to the
+// matrix cores interleaved with the exponentials of tile t (and the tile
+// loads), Y(t) the V^T P^T product of tile t interleaved with the maximum of
+// tile t+1.  The two halves of the workgroup run half a tile apart (one takes
+// the workgroup barrier after Y, the other after X), so on every SIMD one
+// wavefront works through X while the other works through Y.
 #include "kernels.h"
 
 #include <cmath>
 #include <type_traits>
 
-// Workgroup shape per head dimension (wavefronts, K/V ring slots), chosen by
-// measurement on MI355X: d=128 runs 8 wavefronts (256 query rows share each
-// K/V tile, one workgroup per CU), d=64 runs 4 (128 rows, two per CU).
+// Workgroup shape per head dimension, chosen by measurement on MI355X: d=128
+// runs 8 wavefronts (256 query rows share each K/V tile, one workgroup per
+// CU), d=64 runs 4 (128 rows, two per CU).
 #ifndef MIATTN_PREFILL_NW128
 #define MIATTN_PREFILL_NW128 8
 #endif
 #ifndef MIATTN_PREFILL_NW64
 #define MIATTN_PREFILL_NW64 4
-#endif
-#ifndef MIATTN_PREFILL_NS
-#define MIATTN_PREFILL_NS 2
 #endif
 
 namespace miattn {
@@ -95,7 +96,7 @@ constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 __device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u,
                                                                      0u};
 
-template <int D, int NW, int NS>
+template <int D, int NW>
 struct Cfg {
   static constexpr int THREADS = 64 * NW;
   static constexpr int QB = kQW * NW;    // query rows per workgroup
@@ -113,8 +114,7 @@ struct Cfg {
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static_assert(kKT * KSLOTS % 64 == 0 && kKT * VSLOTS % 64 == 0, "split");
   static_assert(KLW + VLW <= 4 * DB, "interleaved loads fit the PV product");
-  static_assert(NS >= 2 && NS <= 4, "ring");
-  static_assert(NS * (KTILE + VTILE) * 2 <= 160 * 1024, "LDS");
+  static_assert((2 * KTILE + 3 * VTILE) * 2 <= 160 * 1024, "LDS");
 };
 
 // Key held in row r of the K tile in LDS.  Rows are in MFMA row order: with
@@ -153,6 +153,18 @@ __device__ inline void barrier_nofence() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// max(x, x of the lane 32 apart), on the VALU: v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second;
+// both start as x, so afterwards one holds x of the lower half and the other
+// x of the upper half in every lane.  Written as inline assembly with two
+// distinct registers: the builtin given the same value twice was folded to
+// a single result.
+__device__ inline float half_swap_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 struct PrefillParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -168,32 +180,27 @@ struct PrefillParams {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
-template <int D, int NW, int NS>
+template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
-  using C = Cfg<D, NW, NS>;
+  using C = Cfg<D, NW>;
   // one LDS object per ring slot: the compiler keeps per-object alias
   // scopes, which lets reads of one slot proceed while another is filled
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[C::KTILE];
   __shared__ __attribute__((aligned(16))) uint16_t Ks1[C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks2[NS > 2 ? C::KTILE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks3[NS > 3 ? C::KTILE : 8];
+
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[C::VTILE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[C::VTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs2[NS > 2 ? C::VTILE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs3[NS > 3 ? C::VTILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[C::VTILE];
   auto kslot = [&](auto s_c) -> uint16_t* {
     constexpr int S = decltype(s_c)::value;
     if constexpr (S == 0) return Ks0;
-    else if constexpr (S == 1) return Ks1;
-    else if constexpr (S == 2) return Ks2;
-    else return Ks3;
+    else return Ks1;
   };
   auto vslot = [&](auto s_c) -> uint16_t* {
     constexpr int S = decltype(s_c)::value;
     if constexpr (S == 0) return Vs0;
     else if constexpr (S == 1) return Vs1;
-    else if constexpr (S == 2) return Vs2;
-    else return Vs3;
+    else return Vs2;
   };
 
   // ---- block -> (batch, head, query block) --------------------------------
@@ -304,11 +311,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     vrow[m] = r;
     voff[m] = r * D + (c < D / 8 ? c * 8 : 0);
   }
-  // Interleaved loads (issued during the PV product): every wave issues
-  // KLW + VLW of them per tile.  A wave without a load number m (uneven
-  // split), and every load of a step whose tiles take the checked path,
-  // reads the zero block into a 1 KB sink: its offset would point past the
-  // tile.
+  // Interleaved loads (issued during X): every wave issues KLW + VLW of
+  // them per tile.  A wave without a load number m (uneven split), and every
+  // load of a step whose tiles take the checked path, reads the zero block
+  // into a 1 KB sink: its offset would point past the tile.
   __shared__ __attribute__((aligned(16))) uint16_t Sink[512];
   auto dma_il = [&](const uint16_t* base, uint16_t* slot, bool real,
                     unsigned off, int i, int nloads) {
@@ -318,9 +324,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
            : (const void*)kZero16,
         (lds_void*)(ok ? slot + i * 512 : Sink), 16, 0, 0);
   };
-  // loads this wave issues per K tile and per V tile
-  const int kl_w = (C::KLOADS - wave + NW - 1) / NW;
-  const int vl_w = (C::VLOADS - wave + NW - 1) / NW;
 
   auto dma_k = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
@@ -396,10 +399,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // slot and the result is dropped).
   // kbi / vbi: tile bases of this step's interleaved K / V loads (into slots
   // SLK / SLV); real_k / real_v: whether they are this step's real loads.
-  auto tile = [&](auto sv_c, auto sk_c, auto slk_c, auto slv_c,
-                  const uint16_t* kbi, const uint16_t* vbi, bool real_k,
-                  bool real_v, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
-    constexpr int SV = decltype(sv_c)::value;
+  // X(t): mask and maximum of tile t's scores `sc`, lazy rescale, and the
+  // S^T product of tile t+1 (K slot SK) into `sn`, interleaved with tile t's
+  // exponentials and with this wave's share of a tile load pair (K into slot
+  // SLK from kbi, V into slot SLV from vbi); P(t) leaves as bf16 in pb.
+  auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, const uint16_t* kbi,
+                   const uint16_t* vbi, bool real_k, bool real_v, int t,
+                   f32x16(&sc)[2], f32x16(&sn)[2], bf16x8(&pb)[2][2]) {
     constexpr int SK = decltype(sk_c)::value;
     const int j0 = t * kKT;
     float mx = mx_pre;
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_swap_max(mx);
     const float tm = (mx == -INFINITY) ? -INFINITY : mx * p.c;
     const bool need = tm > M + kTau;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -470,12 +476,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         sc[emb][er] = e;
         ls[er & 3] += e;
       }
+      // this step's loads, one per MFMA slot
+      if (i < C::KLW)
+        dma_il(kbi, kslot(slk_c), real_k, koff[i], wave + NW * i, C::KLOADS);
+      else if (i < C::KLW + C::VLW)
+        dma_il(vbi, vslot(slv_c), real_v, voff[i - C::KLW],
+               wave + NW * (i - C::KLW), C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);  // VALU
+      if (i < C::KLW + C::VLW)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
     }
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -485,6 +498,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 8; ++e) pv[e] = sc[mb][8 * m + e];
         pb[mb][m] = __builtin_convertvector(pv, bf16x8);
       }
+  };
+
+  // Y(t): O^T += V^T . P^T from V slot SV, interleaved with the maximum of
+  // the next tile's scores `sn`.
+  auto tileY = [&](auto sv_c, const bf16x8(&pb)[2][2],
+                   const f32x16(&sn)[2]) {
     // O^T += V^T . P^T; V operand reads run two MFMAs ahead.
     constexpr int NPV = 4 * C::DB;
     auto vread = [&](int i) {
@@ -518,35 +537,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
                                                          oacc[db], 0, 0, 0);
       mn2[0] = fmaxf(mn2[0], sn[(2 * i) >> 4][(2 * i) & 15]);
       mn2[1] = fmaxf(mn2[1], sn[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
-      // this step's loads, one per MFMA slot
-      if (i < C::KLW)
-        dma_il(kbi, kslot(slk_c), real_k, koff[i], wave + NW * i, C::KLOADS);
-      else if (i < C::KLW + C::VLW)
-        dma_il(vbi, vslot(slv_c), real_v, voff[i - C::KLW],
-               wave + NW * (i - C::KLW), C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (i < C::KLW + C::VLW)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
     }
     mx_pre = fmaxf(mn2[0], mn2[1]);
   };
 
   f32x16 sa[2], sb[2];
+  bf16x8 pb[2][2];
+  // The two halves of the workgroup run half a tile apart: every wave runs
+  // X(t0) Y(t0) X(t0+1) Y(t0+1) ..., but group 0 (waves 0 .. NW/2-1) takes
+  // the workgroup barrier after each Y and group 1 after each X.  So on each
+  // SIMD one wave is in X (S^T MFMAs, exponentials, K reads, tile loads)
+  // while the other is in Y (PV MFMAs, V reads).  Between barriers j-1 and j
+  // (t = t0 + j) group 0 runs X(t) Y(t) and group 1 runs Y(t-1) X(t); they
+  // read K(t+1), V(t) and V(t-1), and X(t) loads each wave's share of K(t+2)
+  // (over K(t), read by X(t-1)) and V(t+1) (over V(t-2), read by Y(t-2)).
+  // K(t) lives in K slot (t - t0) % 2, V(t) in V slot (t - t0) % 3.
+  const bool g1 = wave >= NW / 2;
 
-  // ---- prologue: K(t0 .. t0+NS-1) and V(t0 .. t0+NS-2) in flight ----------
+  // ---- prologue: K(t0), K(t0+1), V(t0) resident, S^T(t0) formed ----------
   if (t1 > t0) {
     dma_k(ic<0>(), t0);
     dma_v(ic<0>(), t0);
     if (t0 + 1 < t1) dma_k(ic<1>(), t0 + 1);
-    if constexpr (NS >= 3) {
-      if (t0 + 1 < t1) dma_v(ic<1>(), t0 + 1);
-      if (t0 + 2 < t1) dma_k(ic<2 % NS>(), t0 + 2);
-    }
-    if constexpr (NS >= 4) {
-      if (t0 + 2 < t1) dma_v(ic<2>(), t0 + 2);
-      if (t0 + 3 < t1) dma_k(ic<3 % NS>(), t0 + 3);
-    }
   }
   wait_vmcnt(0);
   barrier_nofence();
@@ -559,62 +573,48 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   }
   barrier_nofence();
 
-  // Loads this wave issues in the iteration for tile t.
-  auto issued = [&](int t) {
-    return (t + NS - 1 < t1 ? vl_w : 0) + (t + NS < t1 ? kl_w : 0);
-  };
-  // Iteration for tile t = t0 + k, with k % NS == KK: V(t) is in slot KK and
-  // K(t+1) in slot (KK+1) % NS.  It refills V(t+NS-1) into slot
-  // (KK+NS-1) % NS (held V(t-1), done) and K(t+NS) into slot KK (held K(t),
-  // done).
-  auto step = [&](auto kk_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
-    constexpr int KK = decltype(kk_c)::value;
-    constexpr int SLV = (KK + NS - 1) % NS;
-    const int tk = t + NS;      // K tile for slot KK
-    const int tv = t + NS - 1;  // V tile for slot SLV
+  auto step = [&](auto k_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int K = decltype(k_c)::value;
+    constexpr int SLK = K % 2, SLV = (K + 1) % 3;
+    const int tk = t + 2, tv = t + 1;
     const bool whole_k = tk < t1 && (tk + 1) * kKT <= L;
     const bool whole_v = tv < t1 && (tv + 1) * kKT <= L;
-    const bool il = wave_needs(t);  // this wave's loads go inside its tile
+    const bool il = wave_needs(t);  // this wave's loads go inside X(t)
     if (!(il && whole_v) && tv < t1) dma_v(ic<SLV>(), tv);
-    if (!(il && whole_k) && tk < t1) dma_k(ic<KK>(), tk);
+    if (!(il && whole_k) && tk < t1) dma_k(ic<SLK>(), tk);
     if (il) {
       // (a base is only dereferenced when its tile is whole)
-      tile(ic<KK>(), ic<(KK + 1) % NS>(), ic<KK>(), ic<SLV>(),
-           kg + (size_t)(whole_k ? tk : 0) * kKT * D,
-           vg + (size_t)(whole_v ? tv : 0) * kKT * D, whole_k, whole_v, t,
-           sc, sn);
+      tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(),
+            kg + (size_t)(whole_k ? tk : 0) * kKT * D,
+            vg + (size_t)(whole_v ? tv : 0) * kKT * D, whole_k, whole_v, t,
+            sc, sn, pb);
     } else if (t + 1 < t1 && wave_needs(t + 1)) {
-      qk(ic<(KK + 1) % NS>(), sn);
+      qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx_pre = fmaxf(mx_pre, sn[mb][r]);
     }
-    // K(t+2) and V(t+1) were issued in the iteration for tile t+2-NS (or in
-    // the prologue); only the loads of later iterations may stay in flight.
-    int later = 0;
-#pragma unroll
-    for (int d = 0; d < NS - 2; ++d)
-      if (t - d >= t0) later += issued(t - d);
-    wait_vmcnt(later);
-    barrier_nofence();
+    if (g1) {
+      wait_vmcnt(0);
+      barrier_nofence();
+    }
+    if (il) tileY(ic<K % 3>(), pb, sn);
+    if (!g1) {
+      wait_vmcnt(0);
+      barrier_nofence();
+    }
   };
-  // Unrolled by 2*NS: every ring slot index is a compile-time constant and
-  // the two score buffers swap roles without copies.
-  for (int t = t0; t < t1; t += 2 * NS) {
+  // Unrolled by 6: every ring slot index is a compile-time constant and the
+  // two score buffers swap roles without copies.
+  for (int t = t0; t < t1; t += 6) {
     step(ic<0>(), t, sa, sb);
-    if (t + 1 < t1) step(ic<1 % NS>(), t + 1, sb, sa);
-    if (t + 2 < t1) step(ic<2 % NS>(), t + 2, sa, sb);
-    if (t + 3 < t1) step(ic<3 % NS>(), t + 3, sb, sa);
-    if constexpr (NS >= 3) {
-      if (t + 4 < t1) step(ic<4 % NS>(), t + 4, sa, sb);
-      if (t + 5 < t1) step(ic<5 % NS>(), t + 5, sb, sa);
-    }
-    if constexpr (NS >= 4) {
-      if (t + 6 < t1) step(ic<6 % NS>(), t + 6, sa, sb);
-      if (t + 7 < t1) step(ic<7 % NS>(), t + 7, sb, sa);
-    }
+    if (t + 1 < t1) step(ic<1>(), t + 1, sb, sa);
+    if (t + 2 < t1) step(ic<2>(), t + 2, sa, sb);
+    if (t + 3 < t1) step(ic<3>(), t + 3, sb, sa);
+    if (t + 4 < t1) step(ic<4>(), t + 4, sa, sb);
+    if (t + 5 < t1) step(ic<5>(), t + 5, sb, sa);
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -641,13 +641,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int NW, int NS>
+template <int D, int NW>
 void launch(const PrefillParams& p0, hipStream_t stream) {
-  using C = Cfg<D, NW, NS>;
+  using C = Cfg<D, NW>;
   PrefillParams p = p0;
   p.nqb = (p.N + C::QB - 1) / C::QB;
   p.total = p.B * p.Hq * p.nqb;
-  hipLaunchKernelGGL((prefill_kernel<D, NW, NS>), dim3(p.total),
+  hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
 }
 
@@ -677,9 +677,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   if (p.c == 0.f) p.c = 1e-30f;
   p.qsign = (pr.scale < 0.f) ? 0x80008000u : 0u;
   if (pr.d == 128)
-    launch<128, MIATTN_PREFILL_NW128, MIATTN_PREFILL_NS>(p, stream);
+    launch<128, MIATTN_PREFILL_NW128>(p, stream);
   else
-    launch<64, MIATTN_PREFILL_NW64, MIATTN_PREFILL_NS>(p, stream);
+    launch<64, MIATTN_PREFILL_NW64>(p, stream);
   return hipGetLastError();
 }
 
