@@ -43,6 +43,9 @@ BRUTE_CASES = [
     (3, 4, 2, 1, 7, 3, True, 3, True),    # decode with window
     (2, 2, 2, 1, 6, 2, False, 0, False),  # decode without mask
     (1, 2, 1, 4, 4, 5, True, 1, False),   # window of one: self only
+    (3, 4, 2, 5, 12, 3, True, 0, True),   # chunk of 5 against a cache
+    (2, 3, 1, 4, 10, 2, True, 3, True),   # chunk with a window
+    (2, 2, 1, 6, 9, 4, False, 0, True),   # cross-attention, key padding
 ]
 
 
@@ -345,6 +348,67 @@ def check_decode_is_last_row(attn, seed=10):
                                    rtol=1e-14)
 
 
+def check_chunk_is_tail_of_prefill(attn, seed=13):
+    """A chunk of Nq new query rows against a cache of valid length L gives,
+    row for row, causal self-attention over the L tokens at positions
+    L - Nq .. L - 1; a chunk row whose position is negative (L < Nq) sees no
+    key.  Generalises the one-token case."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, N, d, nq = 4, 4, 2, 15, 4, 5
+    q = _rand(rng, B, Hq, N, d)
+    k = _rand(rng, B, Hkv, N, d)
+    v = _rand(rng, B, Hkv, N, d)
+    seqlens = np.array([15, 9, 5, 3])
+    for window in (0, 4):
+        of, lf = attn(q, k, v, scale=0.7, causal=True, window=window,
+                      seqlens=seqlens)
+        qc = np.zeros((B, Hq, nq, d))
+        for b in range(B):
+            for i in range(nq):
+                pos = seqlens[b] - nq + i
+                if pos >= 0:
+                    qc[b, :, i] = q[b, :, pos]
+        oc, lc = attn(qc, k, v, scale=0.7, causal=True, window=window,
+                      seqlens=seqlens)
+        for b in range(B):
+            for i in range(nq):
+                pos = seqlens[b] - nq + i
+                if pos >= 0:
+                    np.testing.assert_allclose(oc[b, :, i], of[b, :, pos],
+                                               rtol=1e-13, atol=1e-14)
+                    np.testing.assert_allclose(lc[b, :, i], lf[b, :, pos],
+                                               rtol=1e-14)
+                else:
+                    assert np.all(oc[b, :, i] == 0)
+                    assert np.all(np.isneginf(lc[b, :, i]))
+
+
+def check_cross_attention_against_torch(attn, seed=14):
+    """Cross-attention (decoder queries against encoder keys and values, no
+    causal mask, Nq != Nk; explainer page, encoder-decoder attention) with
+    key padding equals PyTorch's CPU float64 scaled dot-product attention
+    with a boolean key mask."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, nq, nk, d = 3, 4, 2, 11, 23, 8
+    q = _rand(rng, B, Hq, nq, d)
+    k = _rand(rng, B, Hkv, nk, d)
+    v = _rand(rng, B, Hkv, nk, d)
+    seqlens = np.array([23, 7, 16])
+    o, lse = attn(q, k, v, scale=0.3, causal=False, window=0,
+                  seqlens=seqlens)
+    mask = np.zeros((B, 1, nq, nk), dtype=bool)
+    for b in range(B):
+        mask[b, 0, :, :seqlens[b]] = True
+    kr = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+    vr = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q), kr, vr, attn_mask=torch.from_numpy(mask),
+        scale=0.3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-12)
+
+
 def check_split_combine(attn, seed=11):
     """Splitting the keys into chunks, attending to each chunk alone and
     merging the (o_c, lse_c) pairs with weights exp(lse_c - lse),
@@ -421,6 +485,8 @@ ALL_CHECKS = [
     check_gqa_equals_repeated_mha,
     check_linearity_and_permutation,
     check_decode_is_last_row,
+    check_chunk_is_tail_of_prefill,
+    check_cross_attention_against_torch,
     check_split_combine,
     check_against_torch_sdpa,
 ]

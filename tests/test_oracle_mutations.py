@@ -53,6 +53,12 @@ def _rowpos_top_left(nq, nk, valid_len):
     return live, 0                       # planted: decode query at position 0
 
 
+def _rowpos_chunk_at_end(nq, nk, valid_len):
+    live = valid_len if nq == nk else nq
+    return live, valid_len - 1           # planted: right for one new token,
+                                         # every chunk row past the end
+
+
 def _probs_no_scale(q_rows, k_rows, scale, mask):
     return _real_probabilities(q_rows, k_rows, 1.0, mask)  # planted
 
@@ -92,6 +98,7 @@ MUTANTS = {
     "window_one_too_wide": ("allowed_mask", _mask_window_wide),
     "padding_ignored": ("allowed_mask", _mask_no_padding),
     "decode_top_left": ("row_positions", _rowpos_top_left),
+    "chunk_at_end": ("row_positions", _rowpos_chunk_at_end),
     "scale_dropped": ("probabilities", _probs_no_scale),
     "score_sign_flipped": ("probabilities", _probs_sign),
     "lse_log2": ("probabilities", _probs_lse_log2),
