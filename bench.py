@@ -201,6 +201,8 @@ def main():
     ap.add_argument("--reps", type=int, default=200,
                     help="repetitions of the trimmed-mean latency protocol")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the Nq < Nk workloads (chunks, cross-attention)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device to "
                          "device three times (counter calibration)")
@@ -317,6 +319,39 @@ def main():
     proto_p = reps(lambda i: prefill())
     proto_d = reps(decode)
 
+    # Nq new rows against a longer key sequence: each workload on its own,
+    # `reps` launches, HIP events around each
+    extra = {}
+    if not args.no_extra:
+        for name, seed in (("chunked-prefill-gqa", 17),
+                           ("cross-attention-padded", 18),
+                           ("chunk32-gpt2-causal", 16)):
+            w = synth.by_name(name)
+            xw = synth.make_inputs(w, seed)
+            Xw = dev_in(xw)
+            ow = torch.empty_like(Xw[0])
+            lw = torch.empty(Xw[0].shape[:3], dtype=torch.float32, device=dev)
+
+            def run_w(i, w=w, Xw=Xw, ow=ow, lw=lw):
+                mi.attn(Xw[0], Xw[1], Xw[2], causal=w.causal,
+                        window=w.window, seqlens=Xw[3], out=ow, lse=lw)
+            for i in range(args.warmup):
+                run_w(i)
+            prot = reps(run_w)
+            fl = 4.0 * w.d * allowed_pairs(w, xw["seqlens"]) * w.Hq
+            tf = fl / (prot["trimmed_mean_ms"] * 1e-3) / 1e12
+            extra[name] = {
+                "value": round(tf, 2), "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flop_per_launch": fl,
+                "trimmed_mean_ms": round(prot["trimmed_mean_ms"], 5),
+                "shape": (f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} "
+                          f"Nk={w.Nk} d={w.d} causal={w.causal}"
+                          + (f" L~U[{w.len_lo},{w.len_hi}]" if w.padded
+                             else "")),
+            }
+            del Xw, ow, lw
+
     if args.copy_probe:
         n = (args.copy_probe << 20) // 2
         src = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -379,6 +414,8 @@ def main():
         "fp32_case_avg_ms": round(sum(f32_ms) / K, 5),
         "latency_protocol": {"prefill": proto_p, "decode": proto_d},
     }
+    if extra:
+        line["nq_lt_nk"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wp, xp)
         line["cpu_baseline"]["gpu_over_cpu"] = round(

@@ -20,7 +20,10 @@
  *  - the problem statement Q, K, V in R^{N x d} -> O: the FlashAttention-3
  *    review page (deepmi.me), input data of the core algorithm;
  *  - the one-token generation step against a growing K/V cache: the SpAtten
- *    review, Background - Attention-Based NLP Models (generation stage).
+ *    review, Background - Attention-Based NLP Models (generation stage), and
+ *    its evaluation setting of new tokens after a prompt (EVALUATION);
+ *  - encoder-decoder (cross) attention, decoder queries against the encoder's
+ *    keys and values: the self-attention explainer page, decoder stack.
  *
  * Layout (all buffers contiguous, innermost dimension last, the
  * [batch, heads, n, d] order of the tutorial page's SDPA example):
@@ -31,8 +34,11 @@
  * Semantics (the readings taken where the pages are silent):
  *   G = Hq / Hkv; query head h reads K/V head h / G (contiguous groups).
  *   L_b = clamp(seqlens[b], 0, Nk).  If Nq == Nk the first L_b query rows are
- *   live and row i sits at position i; if Nq == 1 the single query is the last
- *   token and sits at position L_b - 1 (it sees its own key).
+ *   live and row i sits at position i.  If Nq < Nk all Nq rows are live and
+ *   they are the last Nq positions of the sequence: row i sits at position
+ *   L_b - Nq + i ("bottom-right"; with Nq == 1 the single query is the last
+ *   token and sees its own key; a row whose position is negative sees no key
+ *   under the causal mask).  causal == 0 with Nq != Nk is cross-attention.
  *   Query row i may attend to key j iff i is live, j < L_b,
  *   (causal == 0 or j <= pos(i)) and (window <= 0 or pos(i) - j < window).
  *   Masked scores are excluded exactly (-inf), never a finite penalty.
@@ -68,15 +74,15 @@ enum miattn_status {
                                    bf16 decode (Nq == 1) with
                                    Nk > 33553920 */
   MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; window > 0 without
-                                   causal; Nq not in {1, Nk} */
+                                   causal */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
   MIATTN_ERR_NOMEM = -4         /* the decode workspace could not be grown */
 };
 
 /* bf16 q, k, v, o (raw 16-bit bfloat16 storage); float32 lse (may be NULL:
- * not written); int32 seqlens on the device (may be NULL).  Nq == Nk runs the
- * tiled MFMA prefill kernel; Nq == 1 runs the split-K decode kernel followed
- * by the log-sum-exp combine kernel. */
+ * not written); int32 seqlens on the device (may be NULL).  Nq > 1 runs the
+ * tiled MFMA kernel (prefill, chunked prefill, cross-attention); Nq == 1 runs
+ * the split-K decode kernel followed by the log-sum-exp combine kernel. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int causal, int window, const int* seqlens, void* stream);

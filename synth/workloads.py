@@ -1,5 +1,6 @@
-"""The five workload shapes: one fp32 correctness case, three bf16 prefill
-cases and one bf16 decode step.
+"""Workload shapes: one fp32 correctness case, three bf16 prefill cases and
+one bf16 decode step, then three shapes with 1 < Nq < Nk (new rows against a
+cache, cross-attention).
 
 They stand in for the pages' workloads (GPT-2 / BERT / long-context models);
 no dataset or trained weight is used: Q, K and V are i.i.d. normal draws of
@@ -54,6 +55,19 @@ WORKLOADS = (
     # one decode step against a padded KV cache
     Workload("decode-gqa", B=64, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128,
              dtype="bf16", causal=True, len_lo=2048, len_hi=8192),
+    # -- Nq new rows against a longer key sequence (1 < Nq < Nk) --
+    # 32 new tokens after a prompt (the generation setting of the SpAtten
+    # review: 992 prompt tokens, 32 generated), GPT-2-small heads, padded cache
+    Workload("chunk32-gpt2-causal", B=16, Hq=12, Hkv=12, Nq=32, Nk=1024,
+             d=64, dtype="bf16", causal=True, len_lo=512, len_hi=1024),
+    # the last 1024-token chunk of an 8192-token prompt, GQA heads
+    Workload("chunked-prefill-gqa", B=4, Hq=28, Hkv=4, Nq=1024, Nk=8192,
+             d=128, dtype="bf16", causal=True, amp=0.5),
+    # encoder-decoder (cross) attention: 1024 decoder queries against padded
+    # encoder outputs of up to 2048 tokens, no causal mask
+    Workload("cross-attention-padded", B=16, Hq=12, Hkv=12, Nq=1024,
+             Nk=2048, d=64, dtype="bf16", causal=False, len_lo=1024,
+             len_hi=2048),
 )
 
 

@@ -63,7 +63,6 @@ BAD = [
     (dict(d=96), mi.MIATTN_ERR_UNSUPPORTED, "head dim"),
     (dict(d=256), mi.MIATTN_ERR_UNSUPPORTED, "head dim"),
     (dict(window=8, causal=0), mi.MIATTN_ERR_UNSUPPORTED, "causal"),
-    (dict(Nq=32), mi.MIATTN_ERR_UNSUPPORTED, "decode"),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 12, Nk=1 << 12),
      mi.MIATTN_ERR_INVALID, "too large"),
 ]

@@ -121,6 +121,42 @@ def test_config_gpt2_small_causal_padded_all_rows():
     gu.check_full(w.name, w, 2)
 
 
+# ---- Nq new rows against a longer key sequence (1 < Nq < Nk) ---------------
+
+CHUNK_SMALL = [
+    # chunk against a padded cache; some caches shorter than the chunk
+    W("chunk-causal-d128", 3, 4, 2, 70, 300, 128, "bf16", True, len_lo=20,
+      len_hi=300),
+    W("chunk-causal-d64", 2, 6, 3, 33, 200, 64, "bf16", True, len_lo=1,
+      len_hi=200),
+    W("chunk-window-d128", 2, 4, 1, 130, 520, 128, "bf16", True, window=100,
+      len_lo=200, len_hi=520),
+    W("chunk-full-d64", 2, 4, 4, 257, 700, 64, "bf16", True),
+    W("cross-d128", 2, 8, 2, 90, 333, 128, "bf16", False, len_lo=1,
+      len_hi=333),
+    W("cross-d64-full", 1, 4, 2, 129, 300, 64, "bf16", False),
+    W("chunk-fp32", 2, 4, 2, 20, 150, 64, "fp32", True, len_lo=5,
+      len_hi=150),
+    W("cross-fp32", 2, 2, 1, 40, 90, 128, "fp32", False, len_lo=1,
+      len_hi=90),
+]
+
+
+@pytest.mark.parametrize("w", CHUNK_SMALL, ids=lambda w: w.name)
+def test_chunk_and_cross_small(w):
+    gu.check_full(w.name, w, 71)
+
+
+@pytest.mark.parametrize("name,seed", [
+    ("chunk32-gpt2-causal", 16),
+    ("chunked-prefill-gqa", 17),
+    ("cross-attention-padded", 18),
+])
+def test_chunk_and_cross_full_size_sampled(name, seed):
+    w = synth.by_name(name)
+    gu.check_sampled(name, w, seed)
+
+
 @pytest.mark.parametrize("name,seed", [
     ("gpt2-small-causal-padded", 102),
     ("gqa-causal-prefill", 3),

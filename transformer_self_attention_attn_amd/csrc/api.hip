@@ -57,9 +57,6 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
   if (window > 0 && !causal)
     return fail(MIATTN_ERR_UNSUPPORTED,
                 "%s: a window needs the causal mask (one-sided look-back)", fn);
-  if (Nq != 1 && Nq != Nk)
-    return fail(MIATTN_ERR_UNSUPPORTED,
-                "%s: Nq=%d must be 1 (decode) or Nk=%d (prefill)", fn, Nq, Nk);
   // index arithmetic bounds: element offsets are 64-bit, row and block
   // counts are 32-bit
   const long long qrows = (long long)B * Hq * Nq;

@@ -1,4 +1,6 @@
-// Tiled bf16 prefill attention on gfx950 matrix cores (Nq == Nk).
+// Tiled bf16 attention on gfx950 matrix cores for Nq > 1 query rows: the
+// square prefill (Nq == Nk) and a chunk of Nq < Nk new rows against a key/value
+// cache or an encoder output (cross-attention, no causal mask).
 //
 // What is computed: for every (batch b, query head h, live query row i)
 //   s_ij = scale * q_i . k_j            (K/V head h / G, allowed keys j only)
@@ -172,7 +174,7 @@ struct PrefillParams {
   uint16_t* o;
   float* lse;
   const int* seqlens;
-  int B, Hq, Hkv, N, G, nqb, causal, window, total;
+  int B, Hq, Hkv, Nq, Nk, G, nqb, causal, window, total;
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
 };
@@ -222,12 +224,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   const int hk = grp - b * p.Hkv;
   const int h = hk * p.G + hh;
 
-  int L = p.N;
+  int L = p.Nk;
   if (p.seqlens) {
     L = p.seqlens[b];
-    L = L < 0 ? 0 : (L > p.N ? p.N : L);
+    L = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
   }
   // Nq == Nk: the first L rows are live and row i sits at position i.
+  // Nq != Nk: all Nq rows are live and are the last Nq positions of the
+  // sequence, row i at position L - Nq + i (negative when L < Nq: such a row
+  // sees no key under the causal mask).
+  const int Lq = (p.Nq == p.Nk) ? L : p.Nq;
+  const int off = L - Lq;
 
   const int tid = threadIdx.x;
   // wave index as a scalar: load numbers and LDS destinations derived from
@@ -240,30 +247,32 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   const int qw0 = q0 + wave * kQW;
   const int qi = qw0 + ql;
 
-  const size_t qo_base = (size_t)(b * p.Hq + h) * p.N * D;
-  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.N * D;
+  const size_t qo_base = (size_t)(b * p.Hq + h) * p.Nq * D;
+  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
   const uint16_t* kg = p.k + kv_base;
   const uint16_t* vg = p.v + kv_base;
 
   // ---- key ranges ---------------------------------------------------------
-  const bool qlive = qi < L;
-  const int hi = qlive ? (p.causal ? min(L, qi + 1) : L) : 0;  // exclusive
-  const int lo = (qlive && p.window > 0) ? max(0, qi - p.window + 1) : 0;
+  // allowed keys of row qi: lo <= j < hi (empty when hi <= lo)
+  const bool qlive = qi < Lq;
+  const int pos = qi + off;
+  const int hi = qlive ? (p.causal ? min(L, pos + 1) : L) : 0;  // exclusive
+  const int lo = (qlive && p.window > 0) ? max(0, pos - p.window + 1) : 0;
 
-  const int rows_end = min(q0 + C::QB, L);
+  const int rows_end = min(q0 + C::QB, Lq);
   int t0 = 0, t1 = 0;
   if (rows_end > q0) {
-    const int kv_hi = p.causal ? min(L, rows_end) : L;
-    const int kv_lo = p.window > 0 ? max(0, q0 - p.window + 1) : 0;
+    const int kv_hi = max(0, p.causal ? min(L, rows_end + off) : L);
+    const int kv_lo = p.window > 0 ? max(0, q0 + off - p.window + 1) : 0;
     t0 = kv_lo / kKT;
     t1 = (kv_hi + kKT - 1) / kKT;
   }
-  const int wend = min(qw0 + kQW, L);
+  const int wend = min(qw0 + kQW, Lq);
   const bool wlive = wend > qw0;
-  const int w_hi_max = p.causal ? min(L, wend) : L;
-  const int w_hi_min = p.causal ? min(L, qw0 + 1) : L;
-  const int w_lo_min = p.window > 0 ? max(0, qw0 - p.window + 1) : 0;
-  const int w_lo_max = p.window > 0 ? max(0, wend - p.window) : 0;
+  const int w_hi_max = p.causal ? min(L, wend + off) : L;
+  const int w_hi_min = p.causal ? min(L, qw0 + off + 1) : L;
+  const int w_lo_min = p.window > 0 ? max(0, qw0 + off - p.window + 1) : 0;
+  const int w_lo_max = p.window > 0 ? max(0, wend + off - p.window) : 0;
   auto wave_needs = [&](int t) {
     const int j0 = t * kKT;
     return wlive && j0 < w_hi_max && j0 + kKT > w_lo_min;
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 
   // ---- epilogue -----------------------------------------------------------
   const float lt = l + __shfl_xor(l, 32);
-  if (qi < p.N) {
+  if (qi < p.Nq) {
     const bool any = qlive && lt > 0.f;
     const float inv = any ? 1.f / lt : 0.f;
     uint16_t* orow = p.o + qo_base + (size_t)qi * D;
@@ -635,7 +644,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         *reinterpret_cast<bf16x4*>(orow + db * 32 + quad * 8 + 4 * g) = o4;
       }
     if (g == 0 && p.lse) {
-      p.lse[(size_t)(b * p.Hq + h) * p.N + qi] =
+      p.lse[(size_t)(b * p.Hq + h) * p.Nq + qi] =
           any ? (M + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
@@ -645,7 +654,7 @@ template <int D, int NW>
 void launch(const PrefillParams& p0, hipStream_t stream) {
   using C = Cfg<D, NW>;
   PrefillParams p = p0;
-  p.nqb = (p.N + C::QB - 1) / C::QB;
+  p.nqb = (p.Nq + C::QB - 1) / C::QB;
   p.total = p.B * p.Hq * p.nqb;
   hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
@@ -666,7 +675,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   p.B = pr.B;
   p.Hq = pr.Hq;
   p.Hkv = pr.Hkv;
-  p.N = pr.Nq;
+  p.Nq = pr.Nq;
+  p.Nk = pr.Nk;
   p.G = pr.Hq / pr.Hkv;
   p.causal = pr.causal;
   p.window = pr.window;
