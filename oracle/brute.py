@@ -18,7 +18,8 @@ Rows with no allowed key give o_i = 0 and lse_i = -inf.
 import math
 
 
-def _allowed(i, j, nq, nk, valid_len, causal, window):
+def _allowed(i, j, nq, nk, valid_len, causal, window, window_right=0,
+             sinks=0):
     if nq == nk:
         live, pos = valid_len, i
     else:
@@ -27,12 +28,17 @@ def _allowed(i, j, nq, nk, valid_len, causal, window):
         return False
     if causal and j > pos:
         return False
+    if j < sinks:
+        return True
     if window > 0 and pos - j >= window:
+        return False
+    if window_right > 0 and j - pos >= window_right:
         return False
     return True
 
 
-def attention_loops(q, k, v, *, scale, causal=False, window=0, seqlens=None):
+def attention_loops(q, k, v, *, scale, causal=False, window=0, seqlens=None,
+                    window_right=0, sinks=0):
     """q: nested lists [B][Hq][Nq][d]; k, v: [B][Hkv][Nk][d].
 
     Returns (o [B][Hq][Nq][d], lse [B][Hq][Nq]) as nested lists of floats.
@@ -55,7 +61,8 @@ def attention_loops(q, k, v, *, scale, causal=False, window=0, seqlens=None):
             for i in range(nq):
                 scores = {}
                 for j in range(nk):
-                    if _allowed(i, j, nq, nk, vlen, causal, window):
+                    if _allowed(i, j, nq, nk, vlen, causal, window,
+                                window_right, sinks):
                         dot = math.fsum(q[b][h][i][c] * k[b][hk][j][c]
                                         for c in range(d))
                         scores[j] = scale * dot

@@ -34,7 +34,8 @@ def row_positions(nq, nk, valid_len):
     return live, valid_len - live
 
 
-def allowed_mask(nq, nk, valid_len, causal, window, rows=None):
+def allowed_mask(nq, nk, valid_len, causal, window, rows=None, *,
+                 window_right=0, sinks=0):
     """Boolean [len(rows), nk] matrix: may query row i attend to key j?
 
     allowed(i, j) holds iff all of
@@ -47,6 +48,14 @@ def allowed_mask(nq, nk, valid_len, causal, window, rows=None):
         includes the token itself, i.e. the token and the previous window-1
         keys (tutorial page, "Local Window Attention": each token looks only at
         its neighbours; reading: one-sided, causal direction).
+    Two further options (the tutorial page's local window read as a
+    neighbourhood on both sides, and its strategy list's global tokens / the
+    explainer page's attention sink read as keys every query sees):
+      * window_right > 0 => j - pos(i) < window_right (the right limit of a
+        two-sided window; with `window` as the left limit the neighbourhood
+        is pos - window < j < pos + window_right);
+      * sinks > 0: keys j < sinks are allowed whatever the window says (the
+        causal and padding conditions still apply).
     window <= 0 means no window.  The explainer page sets masked scores to a
     "very small negative value (-inf)"; the reading taken here is exact
     exclusion (-inf), never a finite large negative number.
@@ -60,9 +69,14 @@ def allowed_mask(nq, nk, valid_len, causal, window, rows=None):
     ok = (rows[:, None] < live) & (j < valid_len)
     if causal:
         ok &= j <= pos[:, None]
+    win = np.ones_like(ok)
     if window > 0:
-        ok &= (pos[:, None] - j) < window
-    return ok
+        win &= (pos[:, None] - j) < window
+    if window_right > 0:
+        win &= (j - pos[:, None]) < window_right
+    if sinks > 0:
+        win |= j < sinks
+    return ok & win
 
 
 def probabilities(q_rows, k_rows, scale, mask):
@@ -108,13 +122,24 @@ def _head_map(hq, hkv):
     return [h // g for h in range(hq)]
 
 
+def _extra(window_right, sinks):
+    """Keyword arguments for the two optional mask terms, only when used."""
+    kw = {}
+    if window_right > 0:
+        kw["window_right"] = window_right
+    if sinks > 0:
+        kw["sinks"] = sinks
+    return kw
+
+
 def _valid_len(seqlens, b, nk):
     if seqlens is None:
         return nk
     return int(min(max(int(seqlens[b]), 0), nk))
 
 
-def attention(q, k, v, *, scale=None, causal=False, window=0, seqlens=None):
+def attention(q, k, v, *, scale=None, causal=False, window=0, seqlens=None,
+              window_right=0, sinks=0):
     """Full fp64 attention output and log-sum-exp.
 
     Each head is an independent attention (explainer page, "Multi-Head
@@ -142,7 +167,8 @@ def attention(q, k, v, *, scale=None, causal=False, window=0, seqlens=None):
             v64 = v[b, hk].astype(np.float64)
             for r0 in range(0, nq, _ROW_CHUNK):
                 rows = np.arange(r0, min(nq, r0 + _ROW_CHUNK))
-                mask = allowed_mask(nq, nk, vlen, causal, window, rows)
+                mask = allowed_mask(nq, nk, vlen, causal, window, rows,
+                                    **_extra(window_right, sinks))
                 p, l_ = probabilities(q[b, h, rows], k64, scale, mask)
                 # keys at or beyond the valid length are never allowed, so
                 # their probabilities are exactly 0; leave those V rows out of
@@ -153,7 +179,7 @@ def attention(q, k, v, *, scale=None, causal=False, window=0, seqlens=None):
 
 
 def attention_rows(q, k, v, picks, *, scale=None, causal=False, window=0,
-                   seqlens=None):
+                   seqlens=None, window_right=0, sinks=0):
     """Oracle values for selected output rows only.
 
     picks: iterable of (b, h, i).  Returns (o [n, d] fp64, lse [n] fp64) in
@@ -174,7 +200,8 @@ def attention_rows(q, k, v, picks, *, scale=None, causal=False, window=0,
     for n, (b, h, i) in enumerate(picks):
         hk = heads[h]
         vlen = _valid_len(seqlens, b, nk)
-        mask = allowed_mask(nq, nk, vlen, causal, window, [i])
+        mask = allowed_mask(nq, nk, vlen, causal, window, [i],
+                            **_extra(window_right, sinks))
         p, l_ = probabilities(q[b, h, [i]], k[b, hk], scale, mask)
         o[n] = p[0, :vlen] @ v[b, hk, :vlen].astype(np.float64)
         lse[n] = l_[0]

@@ -409,6 +409,138 @@ def check_cross_attention_against_torch(attn, seed=14):
     np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# two-sided windows and sink keys
+
+MASK_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, d, causal, window, window_right, sinks, padded)
+    (2, 2, 1, 9, 9, 3, False, 3, 3, 0, False),   # two-sided neighbourhood
+    (2, 4, 2, 11, 11, 4, False, 2, 4, 2, True),  # asymmetric, sinks, padding
+    (1, 2, 2, 10, 10, 2, True, 3, 0, 2, True),   # causal window + sinks
+    (2, 2, 1, 4, 12, 3, True, 3, 0, 3, True),    # chunk, window + sinks
+    (3, 2, 1, 1, 13, 4, True, 4, 0, 2, True),    # decode, window + sinks
+    (1, 3, 1, 8, 8, 2, False, 0, 2, 1, False),   # right limit only
+]
+
+
+def check_brute_masks(attn, seed=15):
+    rng = np.random.default_rng(seed)
+    for (B, Hq, Hkv, Nq, Nk, d, causal, wl, wr, sk, padded) in MASK_CASES:
+        q = _rand(rng, B, Hq, Nq, d)
+        k = _rand(rng, B, Hkv, Nk, d)
+        v = _rand(rng, B, Hkv, Nk, d)
+        seqlens = rng.integers(0, Nk + 1, size=B) if padded else None
+        scale = float(rng.uniform(0.2, 1.5))
+        o, lse = attn(q, k, v, scale=scale, causal=causal, window=wl,
+                      seqlens=seqlens, window_right=wr, sinks=sk)
+        ob, lb = brute.attention_loops(_tolist(q), _tolist(k), _tolist(v),
+                                       scale=scale, causal=causal, window=wl,
+                                       seqlens=seqlens, window_right=wr,
+                                       sinks=sk)
+        ob = np.array(ob)
+        lb = np.array(lb)
+        assert np.array_equal(np.isinf(lse), np.isinf(lb)), "empty rows differ"
+        fin = np.isfinite(lb)
+        np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+
+
+def check_masks_scale_zero(attn, seed=16):
+    """scale = 0: every allowed key weighs the same, so O_i is the mean of V
+    over the allowed set and lse_i = ln |allowed(i)|; the set is the window
+    [pos-wl+1, pos+wr-1] joined with the sinks [0, s), cut to [0, L) and, if
+    causal, to j <= pos."""
+    rng = np.random.default_rng(seed)
+    B, H, N, d = 2, 2, 14, 3
+    v = _rand(rng, B, H, N, d)
+    q = _rand(rng, B, H, N, d)
+    k = _rand(rng, B, H, N, d)
+    seqlens = np.array([14, 9])
+    for causal, wl, wr, sk in [(False, 3, 2, 2), (True, 4, 0, 3),
+                               (False, 0, 3, 1), (True, 2, 0, 20)]:
+        o, lse = attn(q, k, v, scale=0.0, causal=causal, window=wl,
+                      seqlens=seqlens, window_right=wr, sinks=sk)
+        for b in range(B):
+            L = seqlens[b]
+            for i in range(N):
+                if i >= L:
+                    assert np.all(o[b, :, i] == 0)
+                    continue
+                lo = i - wl + 1 if wl > 0 else 0
+                hi = i + wr if wr > 0 else N
+                keys = set(range(max(lo, 0), min(hi, L)))
+                keys |= set(range(min(sk, L)))
+                if causal:
+                    keys = {j for j in keys if j <= i}
+                js = sorted(keys)
+                np.testing.assert_allclose(o[b, :, i], v[b][:, js].mean(axis=1),
+                                           rtol=1e-13, atol=1e-14)
+                np.testing.assert_allclose(lse[b, :, i], math.log(len(js)),
+                                           rtol=1e-14)
+
+
+def check_masks_extremes(attn, seed=17):
+    """A two-sided window of at least N on both sides equals no window; sinks
+    covering every key equal no window; zero sinks change nothing."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, N, d = 2, 4, 2, 13, 4
+    q = _rand(rng, B, Hq, N, d)
+    k = _rand(rng, B, Hkv, N, d)
+    v = _rand(rng, B, Hkv, N, d)
+    seqlens = np.array([13, 8])
+    o0, l0 = attn(q, k, v, scale=0.5, causal=False, window=0,
+                  seqlens=seqlens)
+    o1, l1 = attn(q, k, v, scale=0.5, causal=False, window=N, seqlens=seqlens,
+                  window_right=N)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    o2, l2 = attn(q, k, v, scale=0.5, causal=False, window=2, seqlens=seqlens,
+                  window_right=2, sinks=N)
+    assert np.array_equal(o0, o2) and np.array_equal(l0, l2)
+    o3, l3 = attn(q, k, v, scale=0.5, causal=True, window=3, seqlens=seqlens)
+    o4, l4 = attn(q, k, v, scale=0.5, causal=True, window=3, seqlens=seqlens,
+                  sinks=0, window_right=0)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    o5, l5 = attn(q, k, v, scale=0.5, causal=False, window=2, seqlens=seqlens,
+                  window_right=2)
+    assert not np.allclose(o0, o5)
+
+
+def check_masks_against_torch(attn, seed=18):
+    """Two-sided windows and sinks against PyTorch's CPU float64 SDPA with a
+    boolean mask built here from index ranges."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, N, d = 2, 4, 2, 31, 8
+    q = _rand(rng, B, Hq, N, d)
+    k = _rand(rng, B, Hkv, N, d)
+    v = _rand(rng, B, Hkv, N, d)
+    seqlens = np.array([31, 17])
+    for causal, wl, wr, sk in [(False, 5, 5, 0), (False, 4, 2, 3),
+                               (True, 6, 0, 2)]:
+        o, lse = attn(q, k, v, scale=0.4, causal=causal, window=wl,
+                      seqlens=seqlens, window_right=wr, sinks=sk)
+        mask = np.zeros((B, 1, N, N), dtype=bool)
+        for b in range(B):
+            L = seqlens[b]
+            for i in range(L):
+                lo = max(0, i - wl + 1) if wl > 0 else 0
+                hi = min(L, i + wr) if wr > 0 else L
+                mask[b, 0, i, lo:hi] = True
+                mask[b, 0, i, :min(sk, L)] = True
+                if causal:
+                    mask[b, 0, i, i + 1:] = False
+        kr = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+        vr = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q), kr, vr, attn_mask=torch.from_numpy(mask),
+            scale=0.4).numpy()
+        live = mask[:, 0].any(axis=-1)
+        for b in range(B):
+            np.testing.assert_allclose(o[b][:, live[b]], ref[b][:, live[b]],
+                                       rtol=1e-11, atol=1e-12)
+
+
 def check_split_combine(attn, seed=11):
     """Splitting the keys into chunks, attending to each chunk alone and
     merging the (o_c, lse_c) pairs with weights exp(lse_c - lse),
@@ -487,6 +619,10 @@ ALL_CHECKS = [
     check_decode_is_last_row,
     check_chunk_is_tail_of_prefill,
     check_cross_attention_against_torch,
+    check_brute_masks,
+    check_masks_scale_zero,
+    check_masks_extremes,
+    check_masks_against_torch,
     check_split_combine,
     check_against_torch_sdpa,
 ]

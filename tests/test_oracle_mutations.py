@@ -14,7 +14,7 @@ _real_allowed = oa.allowed_mask
 _real_rowpos = oa.row_positions
 
 
-def _mask_causal_strict(nq, nk, valid_len, causal, window, rows=None):
+def _mask_causal_strict(nq, nk, valid_len, causal, window, rows=None, **kw):
     if rows is None:
         rows = np.arange(nq)
     rows = np.asarray(rows)
@@ -26,10 +26,10 @@ def _mask_causal_strict(nq, nk, valid_len, causal, window, rows=None):
         ok &= j < pos[:, None]          # planted: excludes the token itself
     if window > 0:
         ok &= (pos[:, None] - j) < window
-    return ok
+    return ok & _optional_terms(pos, j, causal, window, kw)
 
 
-def _mask_window_wide(nq, nk, valid_len, causal, window, rows=None):
+def _mask_window_wide(nq, nk, valid_len, causal, window, rows=None, **kw):
     if rows is None:
         rows = np.arange(nq)
     rows = np.asarray(rows)
@@ -41,11 +41,49 @@ def _mask_window_wide(nq, nk, valid_len, causal, window, rows=None):
         ok &= j <= pos[:, None]
     if window > 0:
         ok &= (pos[:, None] - j) <= window   # planted: one key too many
-    return ok
+    return ok & _optional_terms(pos, j, causal, window, kw)
 
 
-def _mask_no_padding(nq, nk, valid_len, causal, window, rows=None):
-    return _real_allowed(nq, nk, nk, causal, window, rows)  # planted
+def _mask_no_padding(nq, nk, valid_len, causal, window, rows=None, **kw):
+    return _real_allowed(nq, nk, nk, causal, window, rows, **kw)  # planted
+
+
+def _optional_terms(pos, j, causal, window, kw):
+    """The two-sided window and sink terms as the real oracle has them, so
+    that a planted mistake elsewhere stays the only difference.  Returns the
+    keys the window condition removes unless a sink brings them back."""
+    wr = kw.get("window_right", 0)
+    sk = kw.get("sinks", 0)
+    keep = np.ones((pos.shape[0], j.shape[1]), dtype=bool)
+    if wr > 0:
+        keep &= (j - pos[:, None]) < wr
+    if sk > 0:
+        sink = j < sk
+        if causal:
+            sink = sink & (j <= pos[:, None])
+        keep |= sink
+    return keep
+
+
+def _mask_sinks_past_causal(nq, nk, valid_len, causal, window, rows=None,
+                            window_right=0, sinks=0):
+    ok = _real_allowed(nq, nk, valid_len, causal, window, rows,
+                       window_right=window_right, sinks=sinks)
+    if sinks > 0:
+        if rows is None:
+            rows = np.arange(nq)
+        rows = np.asarray(rows)
+        live, _ = _real_rowpos(nq, nk, valid_len)
+        j = np.arange(nk)[None, :]
+        ok |= (rows[:, None] < live) & (j < min(sinks, valid_len))  # planted:
+    return ok                                     # sinks seen past causal
+
+
+def _mask_right_wide(nq, nk, valid_len, causal, window, rows=None,
+                     window_right=0, sinks=0):
+    return _real_allowed(nq, nk, valid_len, causal, window, rows,
+                         window_right=window_right + 1 if window_right > 0
+                         else 0, sinks=sinks)     # planted: one key too many
 
 
 def _rowpos_top_left(nq, nk, valid_len):
@@ -99,6 +137,8 @@ MUTANTS = {
     "padding_ignored": ("allowed_mask", _mask_no_padding),
     "decode_top_left": ("row_positions", _rowpos_top_left),
     "chunk_at_end": ("row_positions", _rowpos_chunk_at_end),
+    "sinks_past_causal": ("allowed_mask", _mask_sinks_past_causal),
+    "window_right_wide": ("allowed_mask", _mask_right_wide),
     "scale_dropped": ("probabilities", _probs_no_scale),
     "score_sign_flipped": ("probabilities", _probs_sign),
     "lse_log2": ("probabilities", _probs_lse_log2),
