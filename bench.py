@@ -49,7 +49,11 @@ KERNEL_SOURCES = {
 
 
 def allowed_pairs(w, seqlens):
-    """Number of allowed (query, key) pairs per head, summed over batch."""
+    """Number of allowed (query, key) pairs per head, summed over batch.
+
+    Row at position pos: keys below hc (valid length; pos + 1 if causal),
+    of those the window [lo, hw) and the sinks [0, sk); the count is the
+    size of the union of the two ranges."""
     import numpy as np
     total = 0
     for b in range(w.B):
@@ -57,10 +61,15 @@ def allowed_pairs(w, seqlens):
         live = L if w.Nq == w.Nk else w.Nq
         i = np.arange(live, dtype=np.int64)
         pos = i + (L - live)
-        hi = np.minimum(L, pos + 1) if w.causal else np.full_like(i, L)
+        hc = np.clip(pos + 1, 0, L) if w.causal else np.full_like(i, L)
         lo = np.maximum(0, pos - w.window + 1) if w.window > 0 else \
             np.zeros_like(i)
-        total += int(np.maximum(hi - lo, 0).sum())
+        hw = np.clip(pos + w.window_right, 0, hc) if w.window_right > 0 \
+            else hc
+        sk = np.minimum(w.sinks, hc)
+        win = np.maximum(hw - lo, 0)
+        both = np.maximum(np.minimum(hw, sk) - lo, 0)
+        total += int((win + sk - both).sum())
     return total
 
 
@@ -319,13 +328,17 @@ def main():
     proto_p = reps(lambda i: prefill())
     proto_d = reps(decode)
 
-    # Nq new rows against a longer key sequence: each workload on its own,
-    # `reps` launches, HIP events around each
-    extra = {}
+    # Nq new rows against a longer key sequence, and the local-window
+    # variants: each workload on its own, `reps` launches, HIP events around
+    # each; decode shapes in GB/s, the others in TFLOP/s
+    extra, masks = {}, {}
     if not args.no_extra:
         for name, seed in (("chunked-prefill-gqa", 17),
                            ("cross-attention-padded", 18),
-                           ("chunk32-gpt2-causal", 16)):
+                           ("chunk32-gpt2-causal", 16),
+                           ("local-window-bidirectional", 19),
+                           ("sliding-window-sinks", 20),
+                           ("decode-window-sinks", 21)):
             w = synth.by_name(name)
             xw = synth.make_inputs(w, seed)
             Xw = dev_in(xw)
@@ -334,22 +347,33 @@ def main():
 
             def run_w(i, w=w, Xw=Xw, ow=ow, lw=lw):
                 mi.attn(Xw[0], Xw[1], Xw[2], causal=w.causal,
-                        window=w.window, seqlens=Xw[3], out=ow, lse=lw)
+                        window=w.window, seqlens=Xw[3], out=ow, lse=lw,
+                        window_right=w.window_right, sinks=w.sinks)
             for i in range(args.warmup):
                 run_w(i)
             prot = reps(run_w)
-            fl = 4.0 * w.d * allowed_pairs(w, xw["seqlens"]) * w.Hq
-            tf = fl / (prot["trimmed_mean_ms"] * 1e-3) / 1e12
-            extra[name] = {
-                "value": round(tf, 2), "unit": "TFLOP/s",
-                "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_flop_per_launch": fl,
-                "trimmed_mean_ms": round(prot["trimmed_mean_ms"], 5),
-                "shape": (f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} "
-                          f"Nk={w.Nk} d={w.d} causal={w.causal}"
-                          + (f" L~U[{w.len_lo},{w.len_hi}]" if w.padded
-                             else "")),
-            }
+            sec = prot["trimmed_mean_ms"] * 1e-3
+            if w.Nq == 1:
+                by = float(decode_bytes(w, xw["seqlens"]))
+                rec = {"value": round(by / sec / 1e9, 1), "unit": "GB/s",
+                       "frac": round(by / sec / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_launch": by}
+            else:
+                fl = 4.0 * w.d * allowed_pairs(w, xw["seqlens"]) * w.Hq
+                rec = {"value": round(fl / sec / 1e12, 2), "unit": "TFLOP/s",
+                       "frac": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "algorithmic_flop_per_launch": fl}
+            rec["trimmed_mean_ms"] = round(prot["trimmed_mean_ms"], 5)
+            rec["shape"] = (
+                f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} "
+                f"d={w.d} causal={w.causal}"
+                + (f" window={w.window}" if w.window else "")
+                + (f" window_right={w.window_right}" if w.window_right
+                   else "")
+                + (f" sinks={w.sinks}" if w.sinks else "")
+                + (f" L~U[{w.len_lo},{w.len_hi}]" if w.padded else ""))
+            local = w.window or w.window_right or w.sinks
+            (masks if local else extra)[name] = rec
             del Xw, ow, lw
 
     if args.copy_probe:
@@ -416,6 +440,8 @@ def main():
     }
     if extra:
         line["nq_lt_nk"] = extra
+    if masks:
+        line["local_windows"] = masks
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wp, xp)
         line["cpu_baseline"]["gpu_over_cpu"] = round(

@@ -69,11 +69,13 @@ extern "C" {
 enum miattn_status {
   MIATTN_OK = 0,
   MIATTN_ERR_INVALID = -1,      /* null pointer, size <= 0, Hq % Hkv != 0,
-                                   Nq > Nk, window < 0, non-finite scale,
+                                   Nq > Nk, window, window_right or sinks
+                                   < 0, non-finite scale,
                                    pointer not 16-byte aligned, size overflow,
                                    bf16 decode (Nq == 1) with
                                    Nk > 33553920 */
-  MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; window > 0 without
+  MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; attn_fwd(_f32):
+                                   window > 0 without
                                    causal */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
   MIATTN_ERR_NOMEM = -4         /* the decode workspace could not be grown */
@@ -92,6 +94,34 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
                  float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, int window, const int* seqlens,
                  void* stream);
+
+/* attn_fwd with the window read on both sides and sink keys: the O(n^2)
+ * tutorial page's local window (Local Window Attention strategy: a token
+ * looks only at nearby tokens, on either side), and the attention sink that
+ * the self-attention explainer page names in its roadmap (data-efficient
+ * attention design) as a way to manage long context windows: the first keys
+ * stay visible to every row whatever the window.  Query row i at
+ * position pos(i) may attend to key j iff i is live, j < L_b,
+ * (causal == 0 or j <= pos(i)) and
+ *   ( (window_left  <= 0 or pos(i) - j < window_left) and
+ *     (window_right <= 0 or j - pos(i) < window_right) )  or  j < sinks.
+ * window_left is attn_fwd's window; a limit <= 0 is no limit.  Unlike
+ * attn_fwd, a window without the causal mask is accepted (a two-sided
+ * neighbourhood).  attn_fwd(..., window, ...) equals
+ * attn_fwd_masked(..., window, 0, 0, ...).  Errors as attn_fwd, plus
+ * MIATTN_ERR_INVALID for a negative window_right or sinks. */
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                    float scale, int causal, int window_left,
+                    int window_right, int sinks, const int* seqlens,
+                    void* stream);
+
+/* attn_fwd_masked with float32 q, k, v, o. */
+int attn_fwd_masked_f32(const float* q, const float* k, const float* v,
+                        float* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                        int Nk, int d, float scale, int causal,
+                        int window_left, int window_right, int sinks,
+                        const int* seqlens, void* stream);
 
 /* Message for the calling thread's most recent non-OK status ("" if none).
  * The pointer stays valid until the thread's next failing call. */

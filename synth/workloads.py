@@ -1,6 +1,7 @@
 """Workload shapes: one fp32 correctness case, three bf16 prefill cases and
 one bf16 decode step, then three shapes with 1 < Nq < Nk (new rows against a
-cache, cross-attention).
+cache, cross-attention) and three local-window variants (a window on both
+sides, a window plus sink keys).
 
 They stand in for the pages' workloads (GPT-2 / BERT / long-context models);
 no dataset or trained weight is used: Q, K and V are i.i.d. normal draws of
@@ -21,7 +22,9 @@ class Workload:
     d: int
     dtype: str            # "fp32" or "bf16"
     causal: bool
-    window: int = 0       # 0 = no window
+    window: int = 0       # 0 = no window (the left limit: pos - j < window)
+    window_right: int = 0  # 0 = no right limit (j - pos < window_right)
+    sinks: int = 0        # keys j < sinks are always kept (within causal/valid)
     len_lo: int = 0       # valid lengths drawn uniformly from [len_lo, len_hi]
     len_hi: int = 0       # (both 0: every sequence is full length)
     amp: float = 1.0      # Q, K, V = amp * N(0, 1)
@@ -68,6 +71,21 @@ WORKLOADS = (
     Workload("cross-attention-padded", B=16, Hq=12, Hkv=12, Nq=1024,
              Nk=2048, d=64, dtype="bf16", causal=False, len_lo=1024,
              len_hi=2048),
+    # -- local windows --
+    # Longformer-style encoder self-attention: each token sees the 256
+    # tokens on either side and itself (no causal mask), 4096-token inputs
+    Workload("local-window-bidirectional", B=4, Hq=12, Hkv=12, Nq=4096,
+             Nk=4096, d=64, dtype="bf16", causal=False, window=257,
+             window_right=257),
+    # the sliding-window shape above with the first 4 keys kept as sinks
+    Workload("sliding-window-sinks", B=2, Hq=16, Hkv=16, Nq=16384,
+             Nk=16384, d=64, dtype="bf16", causal=True, window=1024,
+             sinks=4),
+    # one decode step over a padded cache that keeps a 2048-key window plus
+    # 4 sink keys (the decode-gqa heads, twice the cache length)
+    Workload("decode-window-sinks", B=32, Hq=32, Hkv=8, Nq=1, Nk=16384,
+             d=128, dtype="bf16", causal=True, window=2048, sinks=4,
+             len_lo=4096, len_hi=16384),
 )
 
 

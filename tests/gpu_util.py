@@ -47,7 +47,8 @@ def run_gpu(w, x, *, scale=None, causal=None, window=None, dev_inputs=None):
     o, lse = mi.attn(q, k, v,
                      causal=w.causal if causal is None else causal,
                      window=w.window if window is None else window,
-                     seqlens=sl, scale=w.scale if scale is None else scale)
+                     seqlens=sl, scale=w.scale if scale is None else scale,
+                     window_right=w.window_right, sinks=w.sinks)
     torch.cuda.synchronize()
     return o, lse
 
@@ -86,7 +87,8 @@ def check_full(name, w, seed, **over):
     """All rows against the oracle (sizes where the oracle takes seconds)."""
     say(f"[gpu] {name} seed={seed} shape=B{w.B} Hq{w.Hq} Hkv{w.Hkv} "
         f"Nq{w.Nq} Nk{w.Nk} d{w.d} {w.dtype} causal={w.causal} "
-        f"window={w.window} padded={w.padded} {over}")
+        f"window={w.window}/{w.window_right} sinks={w.sinks} "
+        f"padded={w.padded} {over}")
     x = synth.make_inputs(w, seed)
     o, lse = run_gpu(w, x, **over)
     go, gl = host(o, lse)
@@ -94,7 +96,8 @@ def check_full(name, w, seed, **over):
         x["q32"], x["k32"], x["v32"],
         scale=over.get("scale", w.scale),
         causal=over.get("causal", w.causal),
-        window=over.get("window", w.window), seqlens=x["seqlens"])
+        window=over.get("window", w.window), seqlens=x["seqlens"],
+        window_right=w.window_right, sinks=w.sinks)
     return compare(name, w.dtype, go, gl, ro, rl, vmag=w.amp)
 
 
@@ -135,7 +138,9 @@ def check_sampled(name, w, seed, x=None, o_lse=None):
     gl = lse[idx].cpu().numpy().astype(np.float64)
     ro, rl = oracle.attention_rows(x["q32"], x["k32"], x["v32"], picks,
                                    scale=w.scale, causal=w.causal,
-                                   window=w.window, seqlens=x["seqlens"])
+                                   window=w.window, seqlens=x["seqlens"],
+                                   window_right=w.window_right,
+                                   sinks=w.sinks)
     return compare(name, w.dtype, go, gl, ro, rl, vmag=w.amp)
 
 

@@ -61,12 +61,22 @@ def test_allowed_pairs_matches_mask_count():
                              window=5, len_lo=20, len_hi=37),
               synth.Workload("t", 3, 2, 2, 1, 50, 64, "bf16", True,
                              len_lo=1, len_hi=50),
-              synth.Workload("t", 1, 1, 1, 16, 16, 64, "bf16", False)):
+              synth.Workload("t", 1, 1, 1, 16, 16, 64, "bf16", False),
+              synth.Workload("t", 2, 1, 1, 40, 90, 64, "bf16", True,
+                             window=9, sinks=5, len_lo=1, len_hi=90),
+              synth.Workload("t", 2, 1, 1, 70, 70, 64, "bf16", False,
+                             window=6, window_right=4, sinks=8, len_lo=3,
+                             len_hi=70),
+              synth.Workload("t", 1, 1, 1, 30, 60, 64, "bf16", False,
+                             window_right=7, sinks=40),
+              synth.Workload("t", 3, 1, 1, 1, 77, 64, "bf16", True,
+                             window=10, sinks=12, len_lo=1, len_hi=77)):
         x = synth.make_inputs(w, 11)
         sl = x["seqlens"]
         total = 0
         for b in range(w.B):
             L = w.Nk if sl is None else int(sl[b])
-            m = allowed_mask(w.Nq, w.Nk, L, w.causal, w.window)
+            m = allowed_mask(w.Nq, w.Nk, L, w.causal, w.window,
+                             window_right=w.window_right, sinks=w.sinks)
             total += int(m.sum())
         assert bench.allowed_pairs(w, sl) == total

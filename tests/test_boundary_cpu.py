@@ -79,6 +79,35 @@ def test_rejected_on_host(fn_name, over, code, msg):
     assert fn_name in err and msg in err, err
 
 
+def call_masked(fn, a):
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+              a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+              a["window"], a.get("window_right", 0), a.get("sinks", 0),
+              a["seqlens"], a["stream"])
+
+
+# the masked entry points take every check above except the one-sided
+# window rule (a window without the causal mask is allowed there), plus
+# non-negative right limits and sink counts
+BAD_MASKED = [b for b in BAD if b[2] != "causal"] + [
+    (dict(window_right=-1), mi.MIATTN_ERR_INVALID, "negative"),
+    (dict(sinks=-3), mi.MIATTN_ERR_INVALID, "negative"),
+    (dict(sinks=-1, causal=0, window=8), mi.MIATTN_ERR_INVALID, "negative"),
+]
+
+
+@pytest.mark.parametrize("fn_name", ["attn_fwd_masked",
+                                     "attn_fwd_masked_f32"])
+@pytest.mark.parametrize("over,code,msg", BAD_MASKED,
+                         ids=[str(b[0]) for b in BAD_MASKED])
+def test_masked_rejected_on_host(fn_name, over, code, msg):
+    fn = getattr(mi, fn_name)
+    rc = call_masked(fn, good(**over))
+    assert rc == code
+    err = mi.attn_last_error()
+    assert fn_name in err and msg in err, err
+
+
 def test_decode_key_limit_on_host():
     # the bf16 decode grid covers at most 65535 splits of 512 keys; longer
     # caches are refused before any HIP call

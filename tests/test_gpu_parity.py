@@ -157,6 +157,69 @@ def test_chunk_and_cross_full_size_sampled(name, seed):
     gu.check_sampled(name, w, seed)
 
 
+# ---- two-sided local windows and sink keys (attn_fwd_masked*) --------------
+
+MASK_SMALL = [
+    # window on both sides, no causal mask, padded; tiles cut by both limits
+    W("two-sided-d128", 2, 4, 2, 300, 300, 128, "bf16", False, window=40,
+      window_right=70, len_lo=100, len_hi=300),
+    W("two-sided-d64-wide", 2, 6, 3, 333, 333, 64, "bf16", False,
+      window=130, window_right=129),
+    # right limit only: row i sees keys j < i + window_right
+    W("right-only-d64", 1, 4, 1, 200, 200, 64, "bf16", False,
+      window_right=65),
+    # left limit only without the causal mask: keys j > i - window, all later
+    W("left-only-noncausal-d128", 2, 2, 2, 260, 260, 128, "bf16", False,
+      window=64),
+    # causal window plus sinks: sink tiles and window tiles apart, adjacent
+    # and overlapping
+    W("causal-win-sinks-d64", 2, 6, 3, 600, 600, 64, "bf16", True, window=65,
+      sinks=4, len_lo=1, len_hi=600),
+    W("causal-win-sinks-tile-d128", 2, 4, 2, 520, 520, 128, "bf16", True,
+      window=100, sinks=65, len_lo=200, len_hi=520),
+    W("causal-self-only-sinks-d128", 1, 4, 4, 300, 300, 128, "bf16", True,
+      window=1, sinks=130),
+    W("sinks-past-window-d64", 2, 4, 2, 400, 400, 64, "bf16", True,
+      window=50, sinks=200),
+    # two-sided window with sinks, no causal mask
+    W("two-sided-sinks-d64", 2, 4, 2, 450, 450, 64, "bf16", False, window=33,
+      window_right=31, sinks=7, len_lo=40, len_hi=450),
+    # chunk against a cache with window and sinks
+    W("chunk-win-sinks-d128", 2, 4, 2, 70, 600, 128, "bf16", True,
+      window=100, sinks=10, len_lo=20, len_hi=600),
+    W("cross-two-sided-d64", 2, 4, 2, 150, 400, 64, "bf16", False, window=60,
+      window_right=20, sinks=3, len_lo=10, len_hi=400),
+    # decode: sinks in the first split, the window in the last, the middle
+    # splits dead
+    W("decode-win-sinks-d128", 4, 8, 2, 1, 1300, 128, "bf16", True,
+      window=300, sinks=5, len_lo=1, len_hi=1300),
+    W("decode-win-sinks-d64", 3, 12, 3, 1, 2000, 64, "bf16", True,
+      window=17, sinks=600, len_lo=1, len_hi=2000),
+    # fp32 path
+    W("fp32-two-sided-sinks", 2, 4, 2, 150, 150, 64, "fp32", False, window=20,
+      window_right=30, sinks=3, len_lo=5, len_hi=150),
+    W("fp32-causal-win-sinks", 1, 2, 1, 200, 200, 128, "fp32", True,
+      window=64, sinks=65),
+    W("fp32-decode-win-sinks", 2, 4, 1, 1, 500, 128, "fp32", True,
+      window=100, sinks=7, len_lo=1, len_hi=500),
+]
+
+
+@pytest.mark.parametrize("w", MASK_SMALL, ids=lambda w: w.name)
+def test_masks_small(w):
+    gu.check_full(w.name, w, 81)
+
+
+@pytest.mark.parametrize("name,seed", [
+    ("local-window-bidirectional", 19),
+    ("sliding-window-sinks", 20),
+    ("decode-window-sinks", 21),
+])
+def test_masks_full_size_sampled(name, seed):
+    w = synth.by_name(name)
+    gu.check_sampled(name, w, seed)
+
+
 @pytest.mark.parametrize("name,seed", [
     ("gpt2-small-causal-padded", 102),
     ("gqa-causal-prefill", 3),

@@ -6,9 +6,11 @@ stream, and raises on a non-OK status.  There is no fallback: if the library
 is not built, importing the binding's entry points raises.
 
 Entry points with the C names (raw pointers as Python ints):
-    attn_fwd, attn_fwd_f32, attn_last_error, attn_release
+    attn_fwd, attn_fwd_f32, attn_fwd_masked, attn_fwd_masked_f32,
+    attn_last_error, attn_release
 Convenience wrapper on torch tensors:
-    attn(q, k, v, causal=False, window=0, seqlens=None, scale=None)
+    attn(q, k, v, causal=False, window=0, seqlens=None, scale=None,
+         window_right=0, sinks=0)
 """
 
 import ctypes
@@ -24,7 +26,8 @@ MIATTN_ERR_UNSUPPORTED = -2
 MIATTN_ERR_HIP = -3
 MIATTN_ERR_NOMEM = -4
 
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_last_error", "attn_release")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_masked",
+           "attn_fwd_masked_f32", "attn_last_error", "attn_release")
 
 _lib = None
 
@@ -51,6 +54,11 @@ def load():
     lib.attn_fwd.restype = ci
     lib.attn_fwd_f32.argtypes = sig
     lib.attn_fwd_f32.restype = ci
+    msig = sig[:14] + [ci, ci] + sig[14:]
+    lib.attn_fwd_masked.argtypes = msig
+    lib.attn_fwd_masked.restype = ci
+    lib.attn_fwd_masked_f32.argtypes = msig
+    lib.attn_fwd_masked_f32.restype = ci
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_release.argtypes = []
@@ -74,6 +82,23 @@ def attn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
                                stream or None)
 
 
+def attn_fwd_masked(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                    window_left, window_right, sinks, seqlens, stream):
+    return load().attn_fwd_masked(q, k, v, o, lse or None, B, Hq, Hkv, Nq,
+                                  Nk, d, scale, int(causal), window_left,
+                                  window_right, sinks, seqlens or None,
+                                  stream or None)
+
+
+def attn_fwd_masked_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        causal, window_left, window_right, sinks, seqlens,
+                        stream):
+    return load().attn_fwd_masked_f32(q, k, v, o, lse or None, B, Hq, Hkv,
+                                      Nq, Nk, d, scale, int(causal),
+                                      window_left, window_right, sinks,
+                                      seqlens or None, stream or None)
+
+
 def attn_last_error():
     return load().attn_last_error().decode()
 
@@ -83,13 +108,15 @@ def attn_release():
 
 
 def attn(q, k, v, *, causal=False, window=0, seqlens=None, scale=None,
-         out=None, lse=None, stream=None):
+         out=None, lse=None, stream=None, window_right=0, sinks=0):
     """Attention on torch device tensors.
 
     q: [B, Hq, Nq, d], k/v: [B, Hkv, Nk, d], all bfloat16 or all float32,
     contiguous, on the same GPU.  seqlens: int32 device tensor [B] or None.
     Returns (o, lse) with o like q and lse float32 [B, Hq, Nq].  The default
-    scale is 1/sqrt(d).
+    scale is 1/sqrt(d).  window_right or sinks > 0, or a window without the
+    causal mask, select the masked entry points (window is then the left
+    limit of the neighbourhood).
     """
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -117,10 +144,17 @@ def attn(q, k, v, *, causal=False, window=0, seqlens=None, scale=None,
         sl = seqlens.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
-    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), causal,
-            int(window), sl, stream)
+    bf = q.dtype == torch.bfloat16
+    if window_right or sinks or (window and not causal):
+        fn = attn_fwd_masked if bf else attn_fwd_masked_f32
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), causal,
+                int(window), int(window_right), int(sinks), sl, stream)
+    else:
+        fn = attn_fwd if bf else attn_fwd_f32
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), causal,
+                int(window), sl, stream)
     if rc != MIATTN_OK:
         raise MiattnError(rc, attn_last_error())
     return out, lse

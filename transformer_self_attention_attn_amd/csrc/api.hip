@@ -3,6 +3,7 @@
 // The contract is documented in include/miattn.h.
 #include "miattn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -30,7 +31,8 @@ bool aligned16(const void* p) {
 // Shared checks of attn_fwd and attn_fwd_f32.  No HIP call happens here.
 int validate(const char* fn, const void* q, const void* k, const void* v,
              const void* o, const float* lse, int B, int Hq, int Hkv, int Nq,
-             int Nk, int d, float scale, int causal, int window) {
+             int Nk, int d, float scale, int causal, int window,
+             int window_right, int sinks, bool one_sided) {
   if (!q || !k || !v || !o)
     return fail(MIATTN_ERR_INVALID, "%s: q, k, v and o must be non-null", fn);
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
@@ -43,8 +45,10 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
                 fn, Hq, Hkv);
   if (Nq > Nk)
     return fail(MIATTN_ERR_INVALID, "%s: Nq=%d exceeds Nk=%d", fn, Nq, Nk);
-  if (window < 0)
-    return fail(MIATTN_ERR_INVALID, "%s: window=%d is negative", fn, window);
+  if (window < 0 || window_right < 0 || sinks < 0)
+    return fail(MIATTN_ERR_INVALID,
+                "%s: window=%d, window_right=%d, sinks=%d: none may be "
+                "negative", fn, window, window_right, sinks);
   if (!std::isfinite(scale))
     return fail(MIATTN_ERR_INVALID, "%s: scale is not finite", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -54,7 +58,7 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
   if (d != 64 && d != 128)
     return fail(MIATTN_ERR_UNSUPPORTED, "%s: head dim d=%d (supported: 64, 128)",
                 fn, d);
-  if (window > 0 && !causal)
+  if (one_sided && window > 0 && !causal)
     return fail(MIATTN_ERR_UNSUPPORTED,
                 "%s: a window needs the causal mask (one-sided look-back)", fn);
   // index arithmetic bounds: element offsets are 64-bit, row and block
@@ -105,6 +109,7 @@ int workspace(size_t need, void** out) {
 
 miattn::Problem make_problem(int B, int Hq, int Hkv, int Nq, int Nk, int d,
                              float scale, int causal, int window,
+                             int window_right, int sinks,
                              const int* seqlens) {
   miattn::Problem p;
   p.B = B;
@@ -115,9 +120,47 @@ miattn::Problem make_problem(int B, int Hq, int Hkv, int Nq, int Nk, int d,
   p.d = d;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
-  p.window = window;
+  // a query position lies in [-Nq, Nk) and a key in [0, Nk), so a window
+  // of Nq + Nk or more keeps every key on its side and sinks beyond Nk add
+  // nothing; clamping keeps the kernels' index arithmetic inside int
+  const long long span = (long long)Nq + Nk;
+  p.window = (int)std::min<long long>(window, span);
+  p.window_right = (int)std::min<long long>(window_right, span);
+  p.sinks = std::min(sinks, Nk);
   p.seqlens = seqlens;
   return p;
+}
+
+// bf16 dispatch shared by attn_fwd and attn_fwd_masked (arguments checked)
+int run_bf16(const char* fn, const void* q, const void* k, const void* v,
+             void* o, float* lse, const miattn::Problem& p, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  int rc;
+  if (p.Nq == 1) {
+    if (p.Nk > miattn::decode_max_keys())
+      return fail(MIATTN_ERR_INVALID,
+                  "%s: decode supports at most %d cache rows (Nk=%d)", fn,
+                  miattn::decode_max_keys(), p.Nk);
+    void* ws = nullptr;
+    rc = workspace(miattn::decode_workspace_bytes(p), &ws);
+    if (rc != MIATTN_OK) return rc;
+    e = miattn::launch_decode_bf16(q, k, v, o, lse, p, ws, st);
+  } else {
+    e = miattn::launch_prefill_bf16(q, k, v, o, lse, p, st);
+  }
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
+int run_f32(const char* fn, const float* q, const float* k, const float* v,
+            float* o, float* lse, const miattn::Problem& p, void* stream) {
+  const hipError_t e = miattn::launch_attn_f32(
+      q, k, v, o, lse, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return MIATTN_OK;
 }
 
 }  // namespace
@@ -127,28 +170,28 @@ extern "C" {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int causal, int window, const int* seqlens, void* stream) {
-  int rc = validate("attn_fwd", q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                    causal, window);
+  const int rc = validate("attn_fwd", q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                          scale, causal, window, 0, 0, true);
   if (rc != MIATTN_OK) return rc;
-  const miattn::Problem p =
-      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, seqlens);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (Nq == 1) {
-    if (Nk > miattn::decode_max_keys())
-      return fail(MIATTN_ERR_INVALID,
-                  "attn_fwd: decode supports at most %d cache rows (Nk=%d)",
-                  miattn::decode_max_keys(), Nk);
-    void* ws = nullptr;
-    rc = workspace(miattn::decode_workspace_bytes(p), &ws);
-    if (rc != MIATTN_OK) return rc;
-    e = miattn::launch_decode_bf16(q, k, v, o, lse, p, ws, st);
-  } else {
-    e = miattn::launch_prefill_bf16(q, k, v, o, lse, p, st);
-  }
-  if (e != hipSuccess)
-    return fail(MIATTN_ERR_HIP, "attn_fwd launch: %s", hipGetErrorString(e));
-  return MIATTN_OK;
+  return run_bf16("attn_fwd", q, k, v, o, lse,
+                  make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                               0, 0, seqlens),
+                  stream);
+}
+
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                    float scale, int causal, int window_left,
+                    int window_right, int sinks, const int* seqlens,
+                    void* stream) {
+  const int rc = validate("attn_fwd_masked", q, k, v, o, lse, B, Hq, Hkv, Nq,
+                          Nk, d, scale, causal, window_left, window_right,
+                          sinks, false);
+  if (rc != MIATTN_OK) return rc;
+  return run_bf16("attn_fwd_masked", q, k, v, o, lse,
+                  make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window_left, window_right, sinks, seqlens),
+                  stream);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
@@ -156,16 +199,27 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
                  float scale, int causal, int window, const int* seqlens,
                  void* stream) {
   const int rc = validate("attn_fwd_f32", q, k, v, o, lse, B, Hq, Hkv, Nq, Nk,
-                          d, scale, causal, window);
+                          d, scale, causal, window, 0, 0, true);
   if (rc != MIATTN_OK) return rc;
-  const miattn::Problem p =
-      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, seqlens);
-  const hipError_t e = miattn::launch_attn_f32(
-      q, k, v, o, lse, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess)
-    return fail(MIATTN_ERR_HIP, "attn_fwd_f32 launch: %s",
-                hipGetErrorString(e));
-  return MIATTN_OK;
+  return run_f32("attn_fwd_f32", q, k, v, o, lse,
+                 make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, 0,
+                              0, seqlens),
+                 stream);
+}
+
+int attn_fwd_masked_f32(const float* q, const float* k, const float* v,
+                        float* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                        int Nk, int d, float scale, int causal,
+                        int window_left, int window_right, int sinks,
+                        const int* seqlens, void* stream) {
+  const int rc = validate("attn_fwd_masked_f32", q, k, v, o, lse, B, Hq, Hkv,
+                          Nq, Nk, d, scale, causal, window_left, window_right,
+                          sinks, false);
+  if (rc != MIATTN_OK) return rc;
+  return run_f32("attn_fwd_masked_f32", q, k, v, o, lse,
+                 make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                              window_left, window_right, sinks, seqlens),
+                 stream);
 }
 
 const char* attn_last_error(void) { return g_err; }

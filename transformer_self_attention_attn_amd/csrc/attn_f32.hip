@@ -24,7 +24,7 @@ struct F32Params {
   float* o;
   float* lse;
   const int* seqlens;
-  int B, Hq, Hkv, Nq, Nk, G, causal, window;
+  int B, Hq, Hkv, Nq, Nk, G, causal, window, window_right, sinks;
   float scale;
   long long rows;
 };
@@ -61,8 +61,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
   const int live_rows = (p.Nq == p.Nk) ? L : p.Nq;
   const int pos = i + (L - live_rows);
   const bool live = i < live_rows;
-  const int hi = live ? (p.causal ? min(L, pos + 1) : L) : 0;  // exclusive
+  // allowed keys: [0, sa) (sink keys) and [lo, hi) (the window), both cut
+  // to the causal and padding limit hc
+  const int hc = live ? (p.causal ? min(L, pos + 1) : L) : 0;  // exclusive
   const int lo = (live && p.window > 0) ? max(0, pos - p.window + 1) : 0;
+  const int hi = p.window_right > 0 ? min(hc, pos + p.window_right) : hc;
+  const int sa = min(p.sinks, hc);
 
   const float* qrow = p.q + (size_t)row * D;
   const float* kb = p.k + (size_t)(b * p.Hkv + hk) * p.Nk * D;
@@ -76,35 +80,40 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
   float acc[C];
   for (int c = 0; c < C; ++c) acc[c] = 0.f;
   float m = -INFINITY, l = 0.f;
-  for (int j0 = lo; j0 < hi; j0 += 64) {
-    const int j = j0 + lane;
-    const bool ok = j < hi;
-    float s = -INFINITY;
-    if (ok) {
-      const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * D);
-      float dot = 0.f;
-      for (int c4 = 0; c4 < D / 4; ++c4) {
-        const float4 kk = kr[c4];
-        dot = fmaf(qs[wave][4 * c4 + 0], kk.x, dot);
-        dot = fmaf(qs[wave][4 * c4 + 1], kk.y, dot);
-        dot = fmaf(qs[wave][4 * c4 + 2], kk.z, dot);
-        dot = fmaf(qs[wave][4 * c4 + 3], kk.w, dot);
+  // online softmax over the keys of [jlo, jhi)
+  auto sweep = [&](int jlo, int jhi) {
+    for (int j0 = jlo; j0 < jhi; j0 += 64) {
+      const int j = j0 + lane;
+      const bool ok = j < jhi;
+      float s = -INFINITY;
+      if (ok) {
+        const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * D);
+        float dot = 0.f;
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+          const float4 kk = kr[c4];
+          dot = fmaf(qs[wave][4 * c4 + 0], kk.x, dot);
+          dot = fmaf(qs[wave][4 * c4 + 1], kk.y, dot);
+          dot = fmaf(qs[wave][4 * c4 + 2], kk.z, dot);
+          dot = fmaf(qs[wave][4 * c4 + 3], kk.w, dot);
+        }
+        s = dot * p.scale;
       }
-      s = dot * p.scale;
+      const float mn = fmaxf(m, wave_max(s));  // finite: lane 0 is allowed
+      const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+      const float pj = ok ? expf(s - mn) : 0.f;
+      l = l * alpha + wave_sum(pj);
+      for (int c = 0; c < C; ++c) acc[c] *= alpha;
+      const int nj = min(64, jhi - j0);
+      for (int jj = 0; jj < nj; ++jj) {
+        const float w = __shfl(pj, jj);
+        const float* vr = vb + (size_t)(j0 + jj) * D;
+        for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vr[lane + 64 * c], acc[c]);
+      }
+      m = mn;
     }
-    const float mn = fmaxf(m, wave_max(s));  // finite: lane 0 is allowed
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
-    const float pj = ok ? expf(s - mn) : 0.f;
-    l = l * alpha + wave_sum(pj);
-    for (int c = 0; c < C; ++c) acc[c] *= alpha;
-    const int nj = min(64, hi - j0);
-    for (int jj = 0; jj < nj; ++jj) {
-      const float w = __shfl(pj, jj);
-      const float* vr = vb + (size_t)(j0 + jj) * D;
-      for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vr[lane + 64 * c], acc[c]);
-    }
-    m = mn;
-  }
+  };
+  sweep(0, sa);
+  sweep(max(lo, sa), hi);
   float* orow = p.o + (size_t)row * D;
   const bool any = l > 0.f;
   const float inv = any ? 1.f / l : 0.f;
@@ -132,6 +141,8 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v,
   p.G = pr.Hq / pr.Hkv;
   p.causal = pr.causal;
   p.window = pr.window;
+  p.window_right = pr.window_right;
+  p.sinks = pr.sinks;
   p.scale = pr.scale;
   p.rows = (long long)pr.B * pr.Hq * pr.Nq;
   const unsigned blocks =

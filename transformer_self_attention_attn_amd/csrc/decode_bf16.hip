@@ -64,12 +64,12 @@ struct DecodeParams {
   const int* seqlens;
   float* ws_o;    // [B, Hq, nsplit, D]
   float* ws_lse;  // [B, Hq, nsplit]
-  int B, Hq, Hkv, Nk, G, GB, nhc, window, nsplit;
+  int B, Hq, Hkv, Nk, G, GB, nhc, window, sinks, nsplit;
   float c;  // scale * log2(e)
 };
 
 __device__ inline void key_range(const DecodeParams& p, int b, int& lo,
-                                 int& L) {
+                                 int& L, int& sk) {
   L = p.Nk;
   if (p.seqlens) {
     L = p.seqlens[b];
@@ -77,7 +77,18 @@ __device__ inline void key_range(const DecodeParams& p, int b, int& lo,
   }
   // the query sits at position L - 1: keys j <= L - 1 (causal or not, no key
   // at or past L is valid); a window keeps L - 1 - j < w, i.e. j >= L - w
+  // (a right limit never removes a key here); sink keys j < sinks stay
   lo = p.window > 0 ? max(0, L - p.window) : 0;
+  sk = min(p.sinks, L);
+}
+
+// Lowest allowed key of split s ([c0, c1) = its keys before the window and
+// sink rules): the split holds sink keys [c0, min(c1, sk)) and window keys
+// [max(c0, lo), c1); c1 (no allowed key) when both are empty.
+__device__ inline int split_first_key(int c0, int c1, int lo, int sk) {
+  if (c0 < sk && c0 < c1) return c0;
+  const int a = max(c0, lo);
+  return a < c1 ? a : c1;
 }
 
 template <int W>
@@ -161,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int e = 0; e < 4; ++e) qw[gi][e] = raw[e];
   }
 
-  int lo, L;
-  key_range(p, b, lo, L);
+  int lo, L, sk;
+  key_range(p, b, lo, L, sk);
   const int c0 = s * kChunk;
   const int c1 = min(c0 + kChunk, L);
-  const int a0 = max(c0, lo);
+  const int a0 = split_first_key(c0, c1, lo, sk);
   if (a0 >= c1) return;  // no allowed key here; the combine skips this split
   const int first = (a0 - c0) / RPB;
   const int nb = (c1 - c0 + RPB - 1) / RPB;  // batches first .. nb-1
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         // keep R - 1 batches in flight: refill the slot freed last step
         issue(i + R - 1, kr[(r + R - 1) % R], vr[(r + R - 1) % R]);
         const int key = c0 + i * RPB + grp;
-        const bool ok = key >= a0 && key < c1;
+        const bool ok = key >= a0 && key < c1 && (key >= lo || key < sk);
         float sc[GB];
 #pragma unroll
         for (int gi = 0; gi < GB; ++gi) {
@@ -324,20 +335,27 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
   if (r >= p.B * p.Hq) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int b = r / p.Hq;
-  int lo, L;
-  key_range(p, b, lo, L);
+  int lo, L, sk;
+  key_range(p, b, lo, L, sk);
   const size_t row0 = (size_t)r * p.nsplit;
   uint16_t* orow = p.o + (size_t)r * D + lane * CPL;
-  if (L <= lo) {  // no allowed key
+  if (L <= lo && sk == 0) {  // no allowed key
 #pragma unroll
     for (int e = 0; e < CPL; ++e) orow[e] = 0;
     if (lane == 0 && p.lse) p.lse[r] = -INFINITY;
     return;
   }
-  const int s0 = lo / kChunk;
+  // the splits the split kernel wrote: those holding an allowed key
+  const int s0 = sk > 0 ? 0 : lo / kChunk;
   const int s1 = (L + kChunk - 1) / kChunk;
+  auto live = [&](int s) {
+    const int c0 = s * kChunk;
+    return split_first_key(c0, min(c0 + kChunk, L), lo, sk) <
+           min(c0 + kChunk, L);
+  };
   float m = -INFINITY;
-  for (int s = s0 + lane; s < s1; s += 64) m = fmaxf(m, p.ws_lse[row0 + s]);
+  for (int s = s0 + lane; s < s1; s += 64)
+    if (live(s)) m = fmaxf(m, p.ws_lse[row0 + s]);
   m = wave_max(m);
   float acc[CPL];
 #pragma unroll
@@ -345,6 +363,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
   float wsum = 0.f;
 #pragma unroll 4
   for (int s = s0; s < s1; ++s) {
+    if (!live(s)) continue;  // wave-uniform
     const float w = expf(p.ws_lse[row0 + s] - m);
     wsum += w;
     const float* src = p.ws_o + (row0 + s) * D + lane * CPL;
@@ -414,6 +433,7 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   p.GB = heads_per_block(p.G);
   p.nhc = (p.G + p.GB - 1) / p.GB;
   p.window = pr.window;
+  p.sinks = pr.sinks;
   p.nsplit = (pr.Nk + kChunk - 1) / kChunk;
   p.c = pr.scale * 1.4426950408889634f;
   const size_t rows = (size_t)pr.B * pr.Hq * p.nsplit;

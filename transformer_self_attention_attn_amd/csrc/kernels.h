@@ -12,7 +12,10 @@ namespace miattn {
 struct Problem {
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
-  int causal, window;
+  int causal;
+  int window;        // left limit: pos - window < j (0 = none)
+  int window_right;  // right limit: j < pos + window_right (0 = none)
+  int sinks;         // keys j < sinks allowed whatever the window says
   const int* seqlens;  // device pointer or nullptr
 };
 

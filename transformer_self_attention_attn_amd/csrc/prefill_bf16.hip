@@ -174,7 +174,7 @@ struct PrefillParams {
   uint16_t* o;
   float* lse;
   const int* seqlens;
-  int B, Hq, Hkv, Nq, Nk, G, nqb, causal, window, total;
+  int B, Hq, Hkv, Nq, Nk, G, nqb, causal, window, window_right, sinks, total;
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
 };
@@ -253,33 +253,69 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   const uint16_t* vg = p.v + kv_base;
 
   // ---- key ranges ---------------------------------------------------------
-  // allowed keys of row qi: lo <= j < hi (empty when hi <= lo)
+  // Row qi at position pos may see keys below hc (the valid length, and
+  // pos + 1 under the causal mask); of those, the window keys lo <= j < hw
+  // (left limit pos - j < window, right limit j - pos < window_right, each
+  // off when 0) and the sink keys j < sk.  Every bound is 0 on a dead row.
   const bool qlive = qi < Lq;
   const int pos = qi + off;
-  const int hi = qlive ? (p.causal ? min(L, pos + 1) : L) : 0;  // exclusive
-  const int lo = (qlive && p.window > 0) ? max(0, pos - p.window + 1) : 0;
+  auto cap = [&](int rpos) {  // hc of the row at position rpos
+    return max(0, p.causal ? min(L, rpos + 1) : L);
+  };
+  auto right = [&](int rpos, int h) {  // hw of that row, given hc = h
+    return p.window_right > 0 ? max(0, min(h, rpos + p.window_right)) : h;
+  };
+  auto left = [&](int rpos) {
+    return p.window > 0 ? max(0, rpos - p.window + 1) : 0;
+  };
+  const int hc = qlive ? cap(pos) : 0;
+  const int hw = right(pos, hc);
+  const int lo = qlive ? left(pos) : 0;
+  const int sk = min(p.sinks, hc);
 
+  // Tiles the workgroup visits: the sink tiles [0, ts1), then the window
+  // tiles [tw0, tw1) (merged into one run when they meet).  Step k of the
+  // loop visits tile tile_of(k), k in [0, nt).
   const int rows_end = min(q0 + C::QB, Lq);
-  int t0 = 0, t1 = 0;
+  int nA = 0, tB0 = 0, nt = 0;
   if (rows_end > q0) {
-    const int kv_hi = max(0, p.causal ? min(L, rows_end + off) : L);
-    const int kv_lo = p.window > 0 ? max(0, q0 + off - p.window + 1) : 0;
-    t0 = kv_lo / kKT;
-    t1 = (kv_hi + kKT - 1) / kKT;
+    const int pl = rows_end - 1 + off;  // position of the last live row
+    const int kv_hc = cap(pl);
+    const int kv_hi = right(pl, kv_hc);
+    const int kv_lo = left(q0 + off);
+    int tw0 = kv_lo / kKT, tw1 = (kv_hi + kKT - 1) / kKT;
+    if (kv_hi <= kv_lo) tw0 = tw1 = 0;
+    const int ts1 = (min(p.sinks, kv_hc) + kKT - 1) / kKT;
+    if (ts1 >= tw0) {
+      nA = max(ts1, tw1);
+      nt = nA;
+    } else {
+      nA = ts1;
+      tB0 = tw0;
+      nt = ts1 + (tw1 - tw0);
+    }
   }
+  auto tile_of = [&](int k) { return k < nA ? k : tB0 + (k - nA); };
+
+  // the same bounds over the wave's live rows qw0 .. wend-1: their union
+  // (wave_needs) and their intersection (tile_full: no mask needed)
   const int wend = min(qw0 + kQW, Lq);
   const bool wlive = wend > qw0;
-  const int w_hi_max = p.causal ? min(L, wend + off) : L;
-  const int w_hi_min = p.causal ? min(L, qw0 + off + 1) : L;
-  const int w_lo_min = p.window > 0 ? max(0, qw0 + off - p.window + 1) : 0;
-  const int w_lo_max = p.window > 0 ? max(0, wend + off - p.window) : 0;
+  const int wpf = qw0 + off, wpl = wend - 1 + off;
+  const int w_hc_max = cap(wpl), w_hc_min = cap(wpf);
+  const int w_hi_max = right(wpl, w_hc_max);
+  const int w_hi_min = right(wpf, w_hc_min);
+  const int w_lo_min = left(wpf), w_lo_max = left(wpl);
+  const int w_sk_max = min(p.sinks, w_hc_max);
+  const int w_sk_min = min(p.sinks, w_hc_min);
   auto wave_needs = [&](int t) {
     const int j0 = t * kKT;
-    return wlive && j0 < w_hi_max && j0 + kKT > w_lo_min;
+    return wlive &&
+           ((j0 < w_hi_max && j0 + kKT > w_lo_min) || j0 < w_sk_max);
   };
   auto tile_full = [&](int t) {
     const int j0 = t * kKT;
-    return j0 >= w_lo_max && j0 + kKT <= w_hi_min;
+    return (j0 >= w_lo_max && j0 + kKT <= w_hi_min) || j0 + kKT <= w_sk_min;
   };
 
   // ---- Q^T fragments (B operand), kept in registers -----------------------
@@ -425,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + mb * 32 + g * 16 + r;
-          if (j < lo || j >= hi) sc[mb][r] = -INFINITY;
+          if ((j < lo || j >= hw) && j >= sk) sc[mb][r] = -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -555,25 +591,26 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   f32x16 sa[2], sb[2];
   bf16x8 pb[2][2];
   // The two halves of the workgroup run half a tile apart: every wave runs
-  // X(t0) Y(t0) X(t0+1) Y(t0+1) ..., but group 0 (waves 0 .. NW/2-1) takes
+  // X(0) Y(0) X(1) Y(1) ... over the steps, but group 0 (waves 0 .. NW/2-1) takes
   // the workgroup barrier after each Y and group 1 after each X.  So on each
   // SIMD one wave is in X (S^T MFMAs, exponentials, K reads, tile loads)
   // while the other is in Y (PV MFMAs, V reads).  Between barriers j-1 and j
-  // (t = t0 + j) group 0 runs X(t) Y(t) and group 1 runs Y(t-1) X(t); they
+  // (step t = j) group 0 runs X(t) Y(t) and group 1 runs Y(t-1) X(t); they
   // read K(t+1), V(t) and V(t-1), and X(t) loads each wave's share of K(t+2)
   // (over K(t), read by X(t-1)) and V(t+1) (over V(t-2), read by Y(t-2)).
-  // K(t) lives in K slot (t - t0) % 2, V(t) in V slot (t - t0) % 3.
+  // K and V of step t (tile tile_of(t)) live in K slot t % 2 and V slot
+  // t % 3.
   const bool g1 = wave >= NW / 2;
 
-  // ---- prologue: K(t0), K(t0+1), V(t0) resident, S^T(t0) formed ----------
-  if (t1 > t0) {
-    dma_k(ic<0>(), t0);
-    dma_v(ic<0>(), t0);
-    if (t0 + 1 < t1) dma_k(ic<1>(), t0 + 1);
+  // ---- prologue: K(0), K(1), V(0) resident, S^T(0) formed ----------------
+  if (nt > 0) {
+    dma_k(ic<0>(), tile_of(0));
+    dma_v(ic<0>(), tile_of(0));
+    if (1 < nt) dma_k(ic<1>(), tile_of(1));
   }
   wait_vmcnt(0);
   barrier_nofence();
-  if (t1 > t0 && wave_needs(t0)) {
+  if (nt > 0 && wave_needs(tile_of(0))) {
     qk(ic<0>(), sa);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -585,19 +622,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   auto step = [&](auto k_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int K = decltype(k_c)::value;
     constexpr int SLK = K % 2, SLV = (K + 1) % 3;
-    const int tk = t + 2, tv = t + 1;
-    const bool whole_k = tk < t1 && (tk + 1) * kKT <= L;
-    const bool whole_v = tv < t1 && (tv + 1) * kKT <= L;
-    const bool il = wave_needs(t);  // this wave's loads go inside X(t)
-    if (!(il && whole_v) && tv < t1) dma_v(ic<SLV>(), tv);
-    if (!(il && whole_k) && tk < t1) dma_k(ic<SLK>(), tk);
+    const int tk = t + 2, tv = t + 1;  // steps whose tiles load now
+    const int rt = tile_of(t), rk = tile_of(tk), rv = tile_of(tv);
+    const bool whole_k = tk < nt && (rk + 1) * kKT <= L;
+    const bool whole_v = tv < nt && (rv + 1) * kKT <= L;
+    const bool il = wave_needs(rt);  // this wave's loads go inside X(t)
+    if (!(il && whole_v) && tv < nt) dma_v(ic<SLV>(), rv);
+    if (!(il && whole_k) && tk < nt) dma_k(ic<SLK>(), rk);
     if (il) {
       // (a base is only dereferenced when its tile is whole)
       tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(),
-            kg + (size_t)(whole_k ? tk : 0) * kKT * D,
-            vg + (size_t)(whole_v ? tv : 0) * kKT * D, whole_k, whole_v, t,
+            kg + (size_t)(whole_k ? rk : 0) * kKT * D,
+            vg + (size_t)(whole_v ? rv : 0) * kKT * D, whole_k, whole_v, rt,
             sc, sn, pb);
-    } else if (t + 1 < t1 && wave_needs(t + 1)) {
+    } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
 #pragma unroll
@@ -617,13 +655,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   };
   // Unrolled by 6: every ring slot index is a compile-time constant and the
   // two score buffers swap roles without copies.
-  for (int t = t0; t < t1; t += 6) {
+  for (int t = 0; t < nt; t += 6) {
     step(ic<0>(), t, sa, sb);
-    if (t + 1 < t1) step(ic<1>(), t + 1, sb, sa);
-    if (t + 2 < t1) step(ic<2>(), t + 2, sa, sb);
-    if (t + 3 < t1) step(ic<3>(), t + 3, sb, sa);
-    if (t + 4 < t1) step(ic<4>(), t + 4, sa, sb);
-    if (t + 5 < t1) step(ic<5>(), t + 5, sb, sa);
+    if (t + 1 < nt) step(ic<1>(), t + 1, sb, sa);
+    if (t + 2 < nt) step(ic<2>(), t + 2, sa, sb);
+    if (t + 3 < nt) step(ic<3>(), t + 3, sb, sa);
+    if (t + 4 < nt) step(ic<4>(), t + 4, sa, sb);
+    if (t + 5 < nt) step(ic<5>(), t + 5, sb, sa);
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -680,6 +718,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   p.G = pr.Hq / pr.Hkv;
   p.causal = pr.causal;
   p.window = pr.window;
+  p.window_right = pr.window_right;
+  p.sinks = pr.sinks;
   p.c = fabsf(pr.scale) * 1.4426950408889634f;
   // scale 0: every allowed key weighs the same.  A tiny positive factor keeps
   // masked scores at -inf * c = -inf (weight exactly 0) while every allowed
