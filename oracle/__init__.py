@@ -11,6 +11,10 @@ What it computes (fp64, the textbook definition, no tiling, no online softmax):
     P = row-wise softmax(S)
     O = P V,   lse_i = log sum_j exp(S[i, j])
 
+and, in `sdpa_bwd`, the exact gradients dQ, dK, dV of that function given
+dO, written out by the chain rule (dV = P^T dO, dP = dO V^T, the softmax
+Jacobian for dS, dQ = scale dS K, dK = scale dS^T Q).
+
 Sources (page titles as printed on the pages; see each function for the exact
 passage):
   * "SpAtten: Efficient Sparse Attention Architecture with Cascade Token and
@@ -41,4 +45,5 @@ from .sdpa import (  # noqa: F401
     probabilities,
     row_positions,
 )
+from .sdpa_bwd import attention_backward  # noqa: F401
 from . import brute  # noqa: F401

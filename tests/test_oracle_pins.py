@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import oracle_bwd_checks as obc
 from tests import oracle_checks as oc
 
 
@@ -105,3 +106,8 @@ def test_padding_contents_never_read():
     ob, lb = oracle.attention(b["q32"], b["k32"], b["v32"], scale=w.scale,
                               causal=True, seqlens=b["seqlens"])
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("check", obc.BWD_CHECKS, ids=lambda c: c.__name__)
+def test_backward_oracle_pin(check):
+    check(oracle.attention_backward)
