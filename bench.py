@@ -328,6 +328,38 @@ def main():
     proto_p = reps(lambda i: prefill())
     proto_d = reps(decode)
 
+    # backward pass of the headline prefill: dQ, dK, dV from the forward's
+    # o and lse and a seeded dO (all three kernels of one attn_bwd call);
+    # algorithmic FLOPs 2.5x the forward's (10*d per allowed pair)
+    bwd = None
+    if not args.no_extra:
+        prefill()
+        gout = synth.make_dout(wp, 3)[0].to(dev)
+        gq, gk, gv = (torch.empty_like(P[0]), torch.empty_like(P[1]),
+                      torch.empty_like(P[2]))
+        sptr = stream.cuda_stream
+
+        def backward(i):
+            rc = mi.attn_bwd(P[0].data_ptr(), P[1].data_ptr(),
+                             P[2].data_ptr(), po.data_ptr(), gout.data_ptr(),
+                             pl.data_ptr(), gq.data_ptr(), gk.data_ptr(),
+                             gv.data_ptr(), wp.B, wp.Hq, wp.Hkv, wp.Nq,
+                             wp.Nk, wp.d, wp.scale, 1, 0, 0, 0, 0, sptr)
+            assert rc == mi.MIATTN_OK, mi.attn_last_error()
+        for i in range(args.warmup):
+            backward(i)
+        protb = reps(backward)
+        bfl = 2.5 * flops
+        btf = bfl / (protb["trimmed_mean_ms"] * 1e-3) / 1e12
+        bwd = {"value": round(btf, 2), "unit": "TFLOP/s",
+               "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+               "algorithmic_flop_per_launch": bfl,
+               "trimmed_mean_ms": round(protb["trimmed_mean_ms"], 5),
+               "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128, 4> + "
+                          "bwd_dq_kernel<128, 8>",
+               "workload": "gqa-causal-prefill, dO = N(0,1) seed [3, 1]"}
+        del gout, gq, gk, gv
+
     # Nq new rows against a longer key sequence, and the local-window
     # variants: each workload on its own, `reps` launches, HIP events around
     # each; decode shapes in GB/s, the others in TFLOP/s
@@ -438,6 +470,8 @@ def main():
         "fp32_case_avg_ms": round(sum(f32_ms) / K, 5),
         "latency_protocol": {"prefill": proto_p, "decode": proto_d},
     }
+    if bwd:
+        line["backward"] = bwd
     if extra:
         line["nq_lt_nk"] = extra
     if masks:

@@ -47,12 +47,13 @@
  *   hold NaN.
  *
  * Ownership: every pointer is a device pointer owned by the caller; the
- * library writes only o and lse.  The decode path (Nq == 1) uses a
- * library-owned device workspace per device, allocated on first use (and
- * grown when a larger problem arrives) and released by attn_release().
- * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
- * and never synchronise.  Two concurrent decode calls on one device share the
- * workspace and must be ordered by the caller (same stream).
+ * library writes only its outputs (o and lse; dq, dk and dv for attn_bwd).
+ * The decode path (Nq == 1) and attn_bwd use a library-owned device
+ * workspace per device, allocated on first use (and grown when a larger
+ * problem arrives) and released by attn_release().  Calls are asynchronous on
+ * `stream` (a hipStream_t; NULL = the null stream) and never synchronise.
+ * Two concurrent decode or backward calls on one device share the workspace
+ * and must be ordered by the caller (same stream).
  *
  * Errors: the return value is a status.  Argument checks run on the host
  * before any HIP call, so they are testable without a GPU.  No call aborts or
@@ -78,7 +79,7 @@ enum miattn_status {
                                    window > 0 without
                                    causal */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
-  MIATTN_ERR_NOMEM = -4         /* the decode workspace could not be grown */
+  MIATTN_ERR_NOMEM = -4         /* the workspace could not be grown */
 };
 
 /* bf16 q, k, v, o (raw 16-bit bfloat16 storage); float32 lse (may be NULL:
@@ -123,11 +124,32 @@ int attn_fwd_masked_f32(const float* q, const float* k, const float* v,
                         int window_left, int window_right, int sinks,
                         const int* seqlens, void* stream);
 
+/* Backward pass (bf16): the gradients dq = dL/dq, dk = dL/dk, dv = dL/dv of a
+ * scalar loss L given dout = dL/do, for the function attn_fwd_masked computes
+ * with the same arguments.  The FlashAttention-3 review page names this pass
+ * and its outputs (about 2.5 times the forward FLOPs) without its equations;
+ * the gradient is the exact one of the forward definition, by the chain rule:
+ *   p_ij = exp(scale q_i.k_j - lse_i) on allowed pairs (else 0),
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (dout_i.v_j - dout_i.o_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ * with dk, dv of a K/V head summed over its Hq/Hkv query heads.
+ * Inputs: q, k, v as for attn_fwd_masked; o and lse (float32, required) the
+ * outputs attn_fwd / attn_fwd_masked gave for them; dout like o.  Outputs:
+ * dq like q, dk and dv like k (bf16, fully written: rows of dead queries,
+ * padding keys and keys no row may see get 0).  Accumulation is fp32; P and
+ * dS enter their products rounded to bf16.  Errors as attn_fwd_masked, plus
+ * MIATTN_ERR_INVALID for a null or misaligned dout, lse, dq, dk or dv. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int window_left, int window_right, int sinks,
+             const int* seqlens, void* stream);
+
 /* Message for the calling thread's most recent non-OK status ("" if none).
  * The pointer stays valid until the thread's next failing call. */
 const char* attn_last_error(void);
 
-/* Frees the library-owned decode workspace on every device that has one.
+/* Frees the library-owned workspace on every device that has one.
  * The caller must ensure no decode call is still running. */
 void attn_release(void);
 

@@ -7,6 +7,9 @@ Recipe: numpy Generator(PCG64(seed)); draw, in this order,
      each multiplied by the workload's amplitude;
 then cast to the storage dtype (bf16: round to nearest even, done by torch).
 The fp32 copies returned for the oracle hold exactly the values the GPU sees.
+The output gradient dO of the backward pass comes from its own stream,
+Generator(PCG64([seed, 1])): float32 standard normals of the query shape,
+cast the same way.
 Optionally the padded region (keys at or beyond the valid length, query rows
 beyond the live rows) is overwritten with NaN to prove outputs never read it.
 """
@@ -55,3 +58,21 @@ def make_inputs(w, seed, pad_fill="draw"):
         out[name + "32"] = a if tdt == torch.float32 else \
             t.to(torch.float32).numpy()
     return out
+
+
+def make_dout(w, seed, pad_fill="draw"):
+    """dO for the backward pass: (torch CPU tensor in the storage dtype,
+    numpy float32 copy with the same values).  pad_fill="nan" writes NaN into
+    the rows of dead queries (Nq == Nk, rows at or beyond the valid length,
+    lengths from make_inputs with the same seed)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    a = _draw(rng, (w.B, w.Hq, w.Nq, w.d), 1.0)
+    if pad_fill == "nan" and w.Nq == w.Nk and w.padded:
+        lens = make_inputs(w, seed)["seqlens"]
+        for b in range(w.B):
+            a[b, :, int(lens[b]):] = np.nan
+    elif pad_fill not in ("draw", "nan"):
+        raise ValueError(pad_fill)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    t = torch.from_numpy(a).to(tdt).contiguous()
+    return t, (a if tdt == torch.float32 else t.to(torch.float32).numpy())

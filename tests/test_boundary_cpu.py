@@ -108,6 +108,36 @@ def test_masked_rejected_on_host(fn_name, over, code, msg):
     assert fn_name in err and msg in err, err
 
 
+def call_bwd(a):
+    return mi.attn_bwd(a["q"], a["k"], a["v"], a["o"], a.get("dout", P),
+                       a["lse"], a.get("dq", P), a.get("dk", P),
+                       a.get("dv", P), a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                       a["Nk"], a["d"], a["scale"], a["causal"], a["window"],
+                       a.get("window_right", 0), a.get("sinks", 0),
+                       a["seqlens"], a["stream"])
+
+
+# the backward entry point takes the masked entry points' checks, and needs
+# dout, lse, dq, dk and dv as well
+BAD_BWD = BAD_MASKED + [
+    (dict(dout=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(lse=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(dq=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(dv=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(dk=P + 8), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(dout=P + 2), mi.MIATTN_ERR_INVALID, "aligned"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", BAD_BWD,
+                         ids=[str(b[0]) for b in BAD_BWD])
+def test_backward_rejected_on_host(over, code, msg):
+    rc = call_bwd(good(**over))
+    assert rc == code
+    err = mi.attn_last_error()
+    assert "attn_bwd" in err and msg in err, err
+
+
 def test_decode_key_limit_on_host():
     # the bf16 decode grid covers at most 65535 splits of 512 keys; longer
     # caches are refused before any HIP call

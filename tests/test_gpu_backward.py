@@ -1,0 +1,195 @@
+"""GPU parity of the backward pass: attn_bwd (through the C ABI, on the
+forward's own o and lse) against the fp64 backward oracle.
+
+Tolerance, per gradient tensor (dq, dk, dv), over every element:
+    sum|g - ref| / sum|ref| <= 1e-2   and   max|g - ref| <= 2e-2 * max|ref|.
+Inputs are bf16; the products accumulate in fp32, but P and dS enter their
+products rounded to bf16 (relative error 2^-9 each), delta uses the bf16
+forward output, and the results are rounded to bf16 (2^-9 again).  A gradient
+is a sum of such terms with mixed signs, so its relative error grows where
+the terms cancel; the bound is stated against the tensor's own scale.
+Structural zeros (dead query rows, padding keys, and every dq, dk at scale 0)
+must be exactly 0.  Where the exact gradient is 0 only by cancellation (a
+window of one key: ds = p (dp - delta) with p = 1 and dp = delta in exact
+arithmetic) the kernel keeps the fp32 rounding residue of dp - delta, bounded
+here by 1e-4 absolute.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_self_attention_attn_amd as mi
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+BWD_TOL = dict(rel_l1=1e-2, max_rel=2e-2, cancel_abs=1e-4)
+
+
+def run_fwd_bwd(w, x, dout, scale=None):
+    q, k, v, sl = gu.to_dev(x)
+    sc = w.scale if scale is None else scale
+    kw = dict(causal=w.causal, window=w.window, seqlens=sl, scale=sc,
+              window_right=w.window_right, sinks=w.sinks)
+    o, lse = mi.attn(q, k, v, **kw)
+    do = dout.to(gu.DEV)
+    dq, dk, dv = mi.attn_backward(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def oracle_grads(w, x, dout32, scale=None, b=None, hk=None):
+    """fp64 oracle gradients; with (b, hk) only that batch and K/V head (its
+    G query heads), as arrays with a leading batch and head axis of 1."""
+    q, k, v, d = x["q32"], x["k32"], x["v32"], dout32
+    sl = x["seqlens"]
+    if b is not None:
+        G = w.Hq // w.Hkv
+        hs = slice(hk * G, (hk + 1) * G)
+        q, d = q[b:b + 1, hs], d[b:b + 1, hs]
+        k, v = k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1]
+        sl = None if sl is None else sl[b:b + 1]
+    return oracle.attention_backward(
+        q, k, v, d, scale=w.scale if scale is None else scale,
+        causal=w.causal, window=w.window, seqlens=sl,
+        window_right=w.window_right, sinks=w.sinks)
+
+
+def compare_grad(name, got, ref, exact_zero=True):
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite gradient"
+    err = np.abs(got - ref)
+    mag = float(np.abs(ref).max())
+    rel = float(err.sum() / max(np.abs(ref).sum(), 1e-300))
+    mx = float(err.max())
+    gu.say(f"  {name}: rel_l1={rel:.3e} max_abs={mx:.3e} "
+           f"max|ref|={mag:.3e}")
+    if mag == 0.0:
+        bound = 0.0 if exact_zero else BWD_TOL["cancel_abs"]
+        assert mx <= bound, f"{name}: {mx} where the gradient is 0"
+        return rel, mx
+    assert rel <= BWD_TOL["rel_l1"], f"{name}: rel_l1 {rel}"
+    assert mx <= BWD_TOL["max_rel"] * mag, f"{name}: max_abs {mx}"
+    return rel, mx
+
+
+def check_structural_zeros(w, x, dq, dk, dv):
+    sl = x["seqlens"]
+    for b in range(w.B):
+        L = w.Nk if sl is None else int(sl[b])
+        assert torch.all(dk[b, :, L:] == 0) and torch.all(dv[b, :, L:] == 0)
+        if w.Nq == w.Nk:
+            assert torch.all(dq[b, :, L:] == 0)
+
+
+def check_bwd_full(name, w, seed, scale=None, pad_fill="draw",
+                   exact_zero=True):
+    gu.say(f"[gpu] bwd {name} seed={seed} shape=B{w.B} Hq{w.Hq} Hkv{w.Hkv} "
+           f"Nq{w.Nq} Nk{w.Nk} d{w.d} causal={w.causal} "
+           f"window={w.window}/{w.window_right} sinks={w.sinks} "
+           f"padded={w.padded} scale={scale}")
+    x = synth.make_inputs(w, seed, pad_fill=pad_fill)
+    dout, dout32 = synth.make_dout(w, seed, pad_fill=pad_fill)
+    dq, dk, dv = run_fwd_bwd(w, x, dout, scale)
+    if pad_fill == "nan":
+        # the oracle never reads padded contents either; give it zeros
+        for a in (x["q32"], x["k32"], x["v32"], dout32):
+            np.nan_to_num(a, copy=False, nan=0.0)
+    rq, rk, rv = oracle_grads(w, x, dout32, scale)
+    check_structural_zeros(w, x, dq, dk, dv)
+    compare_grad(f"{name} dq", dq, rq, exact_zero)
+    compare_grad(f"{name} dk", dk, rk, exact_zero)
+    compare_grad(f"{name} dv", dv, rv, exact_zero)
+
+
+BWD_SMALL = [
+    W("bwd-mha-d64-causal", 2, 4, 4, 300, 300, 64, "bf16", True),
+    W("bwd-gqa3-d128-causal-padded", 3, 6, 2, 333, 333, 128, "bf16", True,
+      len_lo=1, len_hi=333),
+    W("bwd-d128-nocausal", 2, 4, 2, 200, 200, 128, "bf16", False),
+    W("bwd-d64-nocausal-padded", 2, 4, 4, 257, 257, 64, "bf16", False,
+      len_lo=10, len_hi=257),
+    W("bwd-mqa7-d128-window", 2, 7, 1, 400, 400, 128, "bf16", True,
+      window=100),
+    W("bwd-d64-window-sinks-padded", 2, 4, 2, 500, 500, 64, "bf16", True,
+      window=65, sinks=4, len_lo=100, len_hi=500),
+    W("bwd-d128-two-sided-padded", 2, 4, 2, 300, 300, 128, "bf16", False,
+      window=40, window_right=70, len_lo=100, len_hi=300),
+    W("bwd-d64-two-sided-sinks", 1, 4, 1, 333, 333, 64, "bf16", False,
+      window=33, window_right=31, sinks=7),
+    W("bwd-chunk-d128-padded", 2, 4, 2, 70, 300, 128, "bf16", True,
+      len_lo=20, len_hi=300),
+    W("bwd-chunk-d64-window-sinks", 2, 4, 2, 100, 520, 64, "bf16", True,
+      window=90, sinks=10, len_lo=50, len_hi=520),
+    W("bwd-cross-d64-padded", 2, 4, 2, 90, 333, 64, "bf16", False,
+      len_lo=1, len_hi=333),
+    W("bwd-decode-d128-padded", 4, 8, 2, 1, 700, 128, "bf16", True,
+      len_lo=1, len_hi=700),
+    W("bwd-below-tile-d128-padded", 3, 2, 1, 17, 17, 128, "bf16", True,
+      len_lo=0, len_hi=17),
+    W("bwd-exact-tile-d64", 1, 1, 1, 128, 128, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("w", BWD_SMALL, ids=lambda w: w.name)
+def test_backward_small(w):
+    check_bwd_full(w.name, w, 91)
+
+
+def test_backward_window_of_one():
+    """Each row sees only itself: dv_j = sum of the group's dO_j, and dq, dk
+    vanish by cancellation."""
+    w = W("bwd-self-only-d128", 1, 4, 2, 130, 130, 128, "bf16", True,
+          window=1)
+    check_bwd_full(w.name, w, 91, exact_zero=False)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09], ids=["scale0", "negscale"])
+def test_backward_scale_edge(scale):
+    w = W("bwd-scale-edge-d128", 2, 4, 2, 200, 200, 128, "bf16", True,
+          len_lo=30, len_hi=200)
+    check_bwd_full(w.name, w, 92, scale=scale)
+
+
+def test_backward_nan_padding_is_never_read():
+    w = W("bwd-nan-pad-d64", 3, 4, 2, 300, 300, 64, "bf16", True, len_lo=1,
+          len_hi=300)
+    check_bwd_full(w.name, w, 93, pad_fill="nan")
+
+
+def test_backward_is_deterministic():
+    w = W("bwd-determinism-d128", 2, 8, 2, 600, 600, 128, "bf16", True,
+          len_lo=200, len_hi=600)
+    x = synth.make_inputs(w, 94)
+    dout, _ = synth.make_dout(w, 94)
+    a = run_fwd_bwd(w, x, dout)
+    b = run_fwd_bwd(w, x, dout)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("name,seed,groups", [
+    ("gqa-causal-prefill", 3, [(0, 0), (3, 3)]),
+    ("gpt2-small-causal-padded", 2, [(0, 0), (15, 11)]),
+    ("sliding-window-sinks", 20, [(1, 5)]),
+])
+def test_backward_full_size_groups(name, seed, groups):
+    """Full-size workload on the GPU; every gradient element of the sampled
+    (batch, K/V head) groups against the oracle run on that group alone."""
+    w = synth.by_name(name)
+    gu.say(f"[gpu] bwd {name} (full size) seed={seed} groups={groups}")
+    x = synth.make_inputs(w, seed)
+    dout, dout32 = synth.make_dout(w, seed)
+    dq, dk, dv = run_fwd_bwd(w, x, dout)
+    check_structural_zeros(w, x, dq, dk, dv)
+    G = w.Hq // w.Hkv
+    for (b, hk) in groups:
+        rq, rk, rv = oracle_grads(w, x, dout32, b=b, hk=hk)
+        hs = slice(hk * G, (hk + 1) * G)
+        compare_grad(f"{name} b{b} hk{hk} dq", dq[b:b + 1, hs], rq)
+        compare_grad(f"{name} b{b} hk{hk} dk", dk[b:b + 1, hk:hk + 1], rk)
+        compare_grad(f"{name} b{b} hk{hk} dv", dv[b:b + 1, hk:hk + 1], rv)

@@ -27,7 +27,8 @@ MIATTN_ERR_HIP = -3
 MIATTN_ERR_NOMEM = -4
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_masked",
-           "attn_fwd_masked_f32", "attn_last_error", "attn_release")
+           "attn_fwd_masked_f32", "attn_bwd", "attn_last_error",
+           "attn_release")
 
 _lib = None
 
@@ -59,6 +60,8 @@ def load():
     lib.attn_fwd_masked.restype = ci
     lib.attn_fwd_masked_f32.argtypes = msig
     lib.attn_fwd_masked_f32.restype = ci
+    lib.attn_bwd.argtypes = [vp] * 9 + [ci] * 6 + [cf] + [ci] * 4 + [vp, vp]
+    lib.attn_bwd.restype = ci
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_release.argtypes = []
@@ -97,6 +100,14 @@ def attn_fwd_masked_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
                                       Nq, Nk, d, scale, int(causal),
                                       window_left, window_right, sinks,
                                       seqlens or None, stream or None)
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+             causal, window_left, window_right, sinks, seqlens, stream):
+    return load().attn_bwd(q, k, v, o, dout, lse or None, dq, dk, dv, B, Hq,
+                           Hkv, Nq, Nk, d, scale, int(causal), window_left,
+                           window_right, sinks, seqlens or None,
+                           stream or None)
 
 
 def attn_last_error():
@@ -158,3 +169,50 @@ def attn(q, k, v, *, causal=False, window=0, seqlens=None, scale=None,
     if rc != MIATTN_OK:
         raise MiattnError(rc, attn_last_error())
     return out, lse
+
+
+def attn_backward(q, k, v, o, lse, dout, *, causal=False, window=0,
+                  seqlens=None, scale=None, window_right=0, sinks=0,
+                  stream=None):
+    """Gradients (dq, dk, dv) of attention on bfloat16 GPU tensors.
+
+    q, k, v, seqlens and the mask arguments as for `attn`; o and lse are what
+    `attn` returned for them, dout the gradient of the loss with respect to
+    o.  Returns new tensors dq like q, dk and dv like k.
+    """
+    import torch
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or \
+                not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v, o, dout must be contiguous 4-d "
+                             "bfloat16 GPU tensors")
+    if lse.dtype != torch.float32 or not lse.is_cuda or \
+            not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or \
+            o.shape != q.shape or dout.shape != q.shape or \
+            tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("shape mismatch between q, k, v, o, lse, dout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sl = 0
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or not seqlens.is_cuda or \
+                seqlens.numel() != B:
+            raise ValueError("seqlens must be an int32 GPU tensor of size B")
+        sl = seqlens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    rc = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                  dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                  float(scale), causal, int(window), int(window_right),
+                  int(sinks), sl, stream)
+    if rc != MIATTN_OK:
+        raise MiattnError(rc, attn_last_error())
+    return dq, dk, dv

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmiattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip",
+           "bwd_bf16.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -72,7 +72,7 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
   return MIATTN_OK;
 }
 
-// ---- decode workspace, one per device -------------------------------------
+// ---- workspace of the decode and backward passes, one per device ---------
 constexpr int kMaxDevices = 64;
 std::mutex g_ws_mu;
 void* g_ws[kMaxDevices] = {};
@@ -98,7 +98,7 @@ int workspace(size_t need, void** out) {
     if (e != hipSuccess) {
       g_ws[dev] = nullptr;
       (void)hipGetLastError();
-      return fail(MIATTN_ERR_NOMEM, "decode workspace of %zu bytes: %s", need,
+      return fail(MIATTN_ERR_NOMEM, "workspace of %zu bytes: %s", need,
                   hipGetErrorString(e));
     }
     g_ws_bytes[dev] = need;
@@ -220,6 +220,35 @@ int attn_fwd_masked_f32(const float* q, const float* k, const float* v,
                  make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal,
                               window_left, window_right, sinks, seqlens),
                  stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int window_left, int window_right, int sinks,
+             const int* seqlens, void* stream) {
+  const char* fn = "attn_bwd";
+  int rc = validate(fn, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                    window_left, window_right, sinks, false);
+  if (rc != MIATTN_OK) return rc;
+  if (!dout || !lse || !dq || !dk || !dv)
+    return fail(MIATTN_ERR_INVALID,
+                "%s: dout, lse, dq, dk and dv must be non-null", fn);
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(MIATTN_ERR_INVALID,
+                "%s: dout, dq, dk and dv must be 16-byte aligned", fn);
+  const miattn::Problem p =
+      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
+                   window_right, sinks, seqlens);
+  void* ws = nullptr;
+  rc = workspace(miattn::bwd_workspace_bytes(p), &ws);
+  if (rc != MIATTN_OK) return rc;
+  const hipError_t e =
+      miattn::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, p, ws,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return MIATTN_OK;
 }
 
 const char* attn_last_error(void) { return g_err; }

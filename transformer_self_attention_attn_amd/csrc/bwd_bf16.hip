@@ -1,0 +1,844 @@
+// Backward pass of bf16 attention on gfx950 matrix cores: dQ, dK and dV of
+// O = softmax(scale * Q K^T + mask) V given dO, the forward output O and its
+// log-sum-exp.  The FlashAttention-3 review page names this pass (dQ, dK, dV;
+// about 2.5 times the forward FLOPs) without printing its equations; what is
+// computed is the exact gradient of the forward function, by the chain rule
+// through its steps:
+//   p_ij  = exp(scale * q_i . k_j - lse_i)         (allowed pairs, else 0)
+//   dV_j  = sum_i p_ij dO_i
+//   dp_ij = dO_i . v_j
+//   ds_ij = p_ij (dp_ij - delta_i),   delta_i = sum_j p_ij dp_ij = dO_i . O_i
+//   dQ_i  = scale * sum_j ds_ij k_j,  dK_j = scale * sum_i ds_ij q_i
+// with K/V gradients summed over the query heads of a group, and zero for
+// padding keys, dead rows and masked pairs.  The mask (causal, valid length,
+// two-sided window, sink keys) and the row positions are those of the forward
+// kernels.
+//
+// Three launches, no atomics (results do not depend on scheduling):
+//   bwd_pre   delta_i from dO and O, and lse_i * log2(e), per query row, into
+//             a workspace padded to 64 rows; a row that sees no key gets
+//             +inf, so every probability of it is exactly 0.
+//   bwd_dkdv  one workgroup per (batch, K/V head, block of 32*NW keys); wave
+//             w owns 32 keys and holds their K and V as MFMA B operands in
+//             registers; the workgroup streams 64-row tiles of Q and dO (with
+//             their lse and delta) of every query head of the group through
+//             LDS, and each wave forms
+//               S  = Q K^T   and  dP = dO V^T   (A = Q / dO rows from LDS)
+//               P, dS in registers (lane = key, 16 consecutive queries)
+//               dV^T += dO^T P   and  dK^T += Q^T dS   (A = transposing LDS
+//                                                      reads of dO / Q)
+//   bwd_dq    one workgroup per (batch, query head, block of 32*NW rows),
+//             shaped like the forward kernel: wave w owns 32 rows and holds
+//             their Q and dO as B operands; 64-key tiles of K and V stream
+//             through LDS and each wave forms
+//               S^T = K Q^T  and  dP^T = V dO^T
+//               dS^T in registers (lane = query, 16 consecutive keys)
+//               dQ^T += K^T dS^T   (A = transposing LDS reads of K)
+// Tiles arrive by 16-byte direct-to-LDS loads into two ring slots per
+// operand, each slot its own LDS object named by a compile-time index; rows
+// past the valid length (or dead query rows) read a block of zeros, so padded
+// contents never enter a product.
+#include "kernels.h"
+
+#include <cmath>
+#include <type_traits>
+
+namespace miattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+constexpr int kRT = 64;    // rows of a streamed tile (queries or keys)
+constexpr int kWR = 32;    // rows a wave owns (keys in dK/dV, queries in dQ)
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies
+constexpr int kBig = 1 << 30;
+
+__device__ __attribute__((aligned(16))) const unsigned kZeroBwd[4] = {0u, 0u,
+                                                                      0u, 0u};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* lse2;   // [B*Hq][Nqp]: lse * log2(e); +inf on rows that see no key
+  float* delta;  // [B*Hq][Nqp]: dO . O; 0 on those rows
+  const int* seqlens;
+  int B, Hq, Hkv, Nq, Nk, Nqp, G, causal, window, window_right, sinks;
+  int nblk, total;  // blocks per (batch, head) and in the grid
+  float c;          // scale * log2(e)
+  float scale;
+};
+
+template <int D>
+struct BCfg {
+  static constexpr int STR = D + 8;           // tile row stride (elements)
+  static constexpr int CH = STR / 8;          // 16-byte chunks per tile row
+  static constexpr int TILE = kRT * STR;      // elements per tile
+  static constexpr int LOADS = kRT * CH / 64; // wave-wide 1 KB loads per tile
+  static constexpr int KS = D / 16;           // k-steps of a D-long product
+  static constexpr int DB = D / 32;           // 32-row blocks of a D^T result
+  static_assert(kRT * CH % 64 == 0, "tile loads");
+};
+
+// Valid length and row positions of batch b: rows i < Lq are live and row i
+// sits at position i + off (Nq == Nk: the first L rows; otherwise the last Nq
+// positions of the sequence).
+struct Seq {
+  int L, Lq, off;
+};
+__device__ inline Seq seq_of(const BwdParams& p, int b) {
+  int L = p.Nk;
+  if (p.seqlens) {
+    L = p.seqlens[b];
+    L = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
+  }
+  const int Lq = (p.Nq == p.Nk) ? L : p.Nq;
+  return {L, Lq, L - Lq};
+}
+
+// Query rows [lo, hi) that may see key j (empty when lo >= hi).  Row i at
+// position pos sees key j < L when pos >= j under the causal mask and, unless
+// j is a sink key, j - window_right < pos < j + window (each limit off when
+// 0).
+__device__ inline void rows_of_key(const BwdParams& p, const Seq& s, int j,
+                                   int& lo, int& hi) {
+  if (j >= s.L) {
+    lo = s.Lq;
+    hi = 0;
+    return;
+  }
+  int plo = p.causal ? j : -kBig;
+  int phi = kBig;
+  if (j >= p.sinks) {
+    if (p.window_right > 0) plo = max(plo, j - p.window_right + 1);
+    if (p.window > 0) phi = j + p.window;
+  }
+  lo = max(0, plo - s.off);
+  hi = min(s.Lq, phi - s.off);
+}
+
+// Keys of the row at position pos (live rows): those below hc, and of them
+// the window keys [lo, hw) and the sink keys [0, sk).
+struct RowKeys {
+  int hc, hw, lo, sk;
+};
+__device__ inline RowKeys keys_of_row(const BwdParams& p, const Seq& s,
+                                      bool live, int pos) {
+  RowKeys r;
+  if (!live) return {0, 0, 0, 0};
+  r.hc = max(0, p.causal ? min(s.L, pos + 1) : s.L);
+  r.hw = p.window_right > 0 ? max(0, min(r.hc, pos + p.window_right)) : r.hc;
+  r.lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  r.sk = min(p.sinks, r.hc);
+  return r;
+}
+
+// Row of a 32-row MFMA A-operand block that holds tile row m: with this order
+// the 32x32 accumulator gives lane group g (lanes 32g .. 32g+31) the 16
+// consecutive tile rows g*16 .. g*16+15 of each 32-row block.
+__device__ inline int mfma_row(int m) {
+  return (m >> 5) * 32 + ((m >> 2) & 1) * 16 + ((m & 31) >> 3) * 4 + (m & 3);
+}
+
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+__device__ inline void barrier_nofence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ inline float wave_max(float x) {
+  for (int s = 32; s > 0; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+__device__ inline int wave_imin(int x) {
+  for (int s = 32; s > 0; s >>= 1) x = min(x, __shfl_xor(x, s));
+  return x;
+}
+__device__ inline int wave_imax(int x) {
+  for (int s = 32; s > 0; s >>= 1) x = max(x, __shfl_xor(x, s));
+  return x;
+}
+
+// Block index -> logical block: consecutive logical blocks share an XCD (and
+// its L2), so blocks of one (batch, K/V head) group meet in one cache.
+__device__ inline int xcd_block(int bid, int n) {
+  const int xcd = bid % kXcds;
+  const int slot = bid / kXcds;
+  const int per = n / kXcds;
+  const int rem = n % kXcds;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+// One wave-wide direct-to-LDS load of a [64][STR] tile: wave load i fills
+// tile bytes [i*1024, +1024); lane l writes 16-byte chunk i*64 + l, i.e.
+// (row r, chunk c) of the padded row.  `row_ok(r)` false -> zeros; pad chunks
+// take the row's first chunk (they are never read).
+template <int D, typename RowOk>
+__device__ inline void tile_load(const uint16_t* base, uint16_t* tile, int i,
+                                 int lane, RowOk row_ok) {
+  using C = BCfg<D>;
+  const int s = i * 64 + lane;
+  const int r = s / C::CH;
+  const int c = s - r * C::CH;
+  const void* src = row_ok(r) ? (const void*)(base + (size_t)r * D +
+                                              (c < D / 8 ? c * 8 : 0))
+                              : (const void*)kZeroBwd;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + i * 512), 16, 0,
+                                   0);
+}
+
+// A operand of X^T (X a [64][STR] tile in LDS): for the 32 columns
+// db*32 .. +31 (one per lane mod 32) the 8 tile rows row0 .. row0+3 and
+// row0+4 .. row0+7 of this lane's half, read with the transposing LDS read.
+template <int STR>
+__device__ inline bf16x8 tr_read(const uint16_t* tile, int lane_off, int row0,
+                                 int db) {
+  bf16x8 a;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint16_t* ptr = tile + lane_off + (row0 + 4 * half) * STR + db * 32;
+    const i16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a[4 * half + e] = __builtin_bit_cast(__bf16, (short)r4[e]);
+  }
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_pre: one 64-lane wave covers 64*8/D rows; D/8 lanes per row.
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const long long gw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long row = gw * RPW + lane / LPR;  // over B*Hq*Nqp
+  const long long total = (long long)p.B * p.Hq * p.Nqp;
+  const bool valid = row < total;
+  const int bh = valid ? (int)(row / p.Nqp) : 0;
+  const int i = valid ? (int)(row - (long long)bh * p.Nqp) : 0;
+  const Seq s = seq_of(p, bh / p.Hq);
+  float lse = -INFINITY;
+  if (valid && i < s.Lq) lse = p.lse[(size_t)bh * p.Nq + i];
+  const bool live = valid && i < s.Lq && lse > -INFINITY;
+  float acc = 0.f;
+  if (live) {
+    const size_t off = ((size_t)bh * p.Nq + i) * D + (lane % LPR) * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16),
+                 acc);
+      acc = fmaf(__uint_as_float(a[e] & 0xffff0000u),
+                 __uint_as_float(b[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int x = 1; x < LPR; x <<= 1) acc += __shfl_xor(acc, x);
+  if (valid && lane % LPR == 0) {
+    p.delta[row] = live ? acc : 0.f;
+    p.lse2[row] = live ? lse * 1.4426950408889634f : INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dkdv
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
+    BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int KB = kWR * NW;  // keys per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t Qs0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Os0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Os1[C::TILE];
+  __shared__ __attribute__((aligned(16))) float Ls0[kRT];
+  __shared__ __attribute__((aligned(16))) float Ls1[kRT];
+  __shared__ __attribute__((aligned(16))) float Ds0[kRT];
+  __shared__ __attribute__((aligned(16))) float Ds1[kRT];
+  auto qslot = [&](auto s) -> uint16_t* {
+    if constexpr (decltype(s)::value == 0) return Qs0; else return Qs1;
+  };
+  auto oslot = [&](auto s) -> uint16_t* {
+    if constexpr (decltype(s)::value == 0) return Os0; else return Os1;
+  };
+  auto lslot = [&](auto s) -> float* {
+    if constexpr (decltype(s)::value == 0) return Ls0; else return Ls1;
+  };
+  auto dslot = [&](auto s) -> float* {
+    if constexpr (decltype(s)::value == 0) return Ds0; else return Ds1;
+  };
+
+  // (batch, K/V head, key block), key blocks of one group adjacent; within a
+  // group the low key blocks (more query rows under the causal mask) first
+  const int lid = xcd_block(blockIdx.x, p.total);
+  const int grp = lid / p.nblk;
+  const int kb = lid - grp * p.nblk;
+  const int b = grp / p.Hkv;
+  const int hk = grp - b * p.Hkv;
+  const Seq s = seq_of(p, b);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int kl = lane & 31;
+  const int g = lane >> 5;
+  const int k0 = kb * KB;
+  const int kw0 = k0 + wave * kWR;
+  const int j = kw0 + kl;  // this lane's key
+
+  // rows that may see this lane's key, and over the wave: their hull (a tile
+  // outside it is skipped) and their intersection (a tile inside it needs no
+  // mask)
+  int rlo, rhi;
+  rows_of_key(p, s, j, rlo, rhi);
+  const bool kne = rlo < rhi;
+  const int w_lo_min = wave_imin(kne ? rlo : kBig);
+  const int w_hi_max = wave_imax(kne ? rhi : -kBig);
+  const int w_lo_max = wave_imax(rlo);
+  const int w_hi_min = wave_imin(rhi);
+  // the workgroup's hull: the lowest key's first row and, unless the block
+  // holds a sink key, the last valid key's end row
+  int t0 = 0, nt = 0;
+  if (k0 < s.L) {
+    const int k1 = min(k0 + KB, s.L);
+    int a_lo, a_hi, b_lo, b_hi;
+    rows_of_key(p, s, k0, a_lo, a_hi);
+    rows_of_key(p, s, k1 - 1, b_lo, b_hi);
+    const int hi = k0 < p.sinks ? s.Lq : max(a_hi, b_hi);
+    if (hi > a_lo) {
+      t0 = a_lo / kRT;
+      nt = (hi + kRT - 1) / kRT - t0;
+    }
+  }
+  const int nsteps = nt * p.G;  // (query head, tile) pairs
+  auto wave_needs = [&](int t) {
+    const int r0 = t * kRT;
+    return r0 < w_hi_max && r0 + kRT > w_lo_min;
+  };
+  auto tile_full = [&](int t) {
+    const int r0 = t * kRT;
+    return r0 >= w_lo_max && r0 + kRT <= w_hi_min;
+  };
+
+  // K and V of this lane's key as B operands (8 consecutive columns per
+  // k-step), zero past the valid length
+  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
+  bf16x8 kf[C::KS], vf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+    if (j < s.L) {
+      rk = *reinterpret_cast<const u32x4*>(p.k + kv_base + (size_t)j * D +
+                                           16 * ks + 8 * g);
+      rv = *reinterpret_cast<const u32x4*>(p.v + kv_base + (size_t)j * D +
+                                           16 * ks + 8 * g);
+    }
+    kf[ks] = __builtin_bit_cast(bf16x8, rk);
+    vf[ks] = __builtin_bit_cast(bf16x8, rv);
+  }
+
+  f32x16 dka[C::DB], dva[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dka[db][r] = 0.f;
+      dva[db][r] = 0.f;
+    }
+
+  // lane offsets of the LDS operand reads
+  const int grp16 = lane >> 4;
+  const int i16 = lane & 15;
+  const int tr_off = (i16 >> 2) * C::STR + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  int arow[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+    arow[mb] = mfma_row(mb * 32 + kl) * C::STR + 8 * g;
+
+  // loads of step u (query head hk*G + u / nt, tile t0 + u % nt) into slot S
+  auto issue = [&](auto slot_c, int u) {
+    const int h = hk * p.G + u / nt;
+    const int t = t0 + u % nt;
+    const int r0 = t * kRT;
+    const size_t bh = (size_t)b * p.Hq + h;
+    const uint16_t* qb = p.q + (bh * p.Nq + r0) * D;
+    const uint16_t* ob = p.dout + (bh * p.Nq + r0) * D;
+    auto ok = [&](int r) { return r0 + r < s.Lq; };
+    constexpr int NL = 2 * C::LOADS + 2;
+#pragma unroll
+    for (int m = 0; m < (NL + NW - 1) / NW; ++m) {
+      const int u2 = wave + NW * m;
+      if (u2 < C::LOADS) {
+        tile_load<D>(qb, qslot(slot_c), u2, lane, ok);
+      } else if (u2 < 2 * C::LOADS) {
+        tile_load<D>(ob, oslot(slot_c), u2 - C::LOADS, lane, ok);
+      } else if (u2 == 2 * C::LOADS) {
+        __builtin_amdgcn_global_load_lds(p.lse2 + bh * p.Nqp + r0 + lane,
+                                         (lds_void*)lslot(slot_c), 4, 0, 0);
+      } else if (u2 == 2 * C::LOADS + 1) {
+        __builtin_amdgcn_global_load_lds(p.delta + bh * p.Nqp + r0 + lane,
+                                         (lds_void*)dslot(slot_c), 4, 0, 0);
+      }
+    }
+  };
+
+  auto compute = [&](auto slot_c, int u) {
+    const int t = t0 + u % nt;
+    if (!wave_needs(t)) return;
+    const uint16_t* Qt = qslot(slot_c);
+    const uint16_t* Ot = oslot(slot_c);
+    const float* Lt = lslot(slot_c);
+    const float* Dt = dslot(slot_c);
+    // S = Q K^T and dP = dO V^T: lane (key, g) holds tile rows
+    // mb*32 + 16g + r
+    f32x16 sa[2], pa[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sa[mb][r] = 0.f;
+        pa[mb][r] = 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Qt + arow[mb] + 16 * ks);
+        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sa[mb], 0,
+                                                         0, 0);
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Ot + arow[mb] + 16 * ks);
+        pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], pa[mb], 0,
+                                                         0, 0);
+      }
+    // P and dS; rows outside this key's range are masked (partial tiles)
+    const bool full = tile_full(t);
+    const int r0 = t * kRT;
+    bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 =
+            *reinterpret_cast<const f32x4*>(Lt + mb * 32 + 16 * g + 4 * q4);
+        const f32x4 d4 =
+            *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l4[e]));
+          if (!full) {
+            const int i = r0 + mb * 32 + 16 * g + r;
+            if (i < rlo || i >= rhi) pr = 0.f;
+          }
+          pv[r] = pr;
+          dsv[r] = pr * (pa[mb][r] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        f32x8 x, y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = pv[8 * m2 + e];
+          y[e] = dsv[8 * m2 + e];
+        }
+        pb[mb][m2] = __builtin_convertvector(x, bf16x8);
+        sb[mb][m2] = __builtin_convertvector(y, bf16x8);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int row0 = mb * 32 + 16 * g + 8 * m2;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 a = tr_read<C::STR>(Ot, tr_off, row0, db);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][m2],
+                                                            dva[db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 a = tr_read<C::STR>(Qt, tr_off, row0, db);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
+                                                            dka[db], 0, 0, 0);
+        }
+      }
+  };
+
+  if (nsteps > 0) {
+    issue(ic<0>(), 0);
+    wait_vm0();
+    barrier_nofence();
+    auto step = [&](auto slot_c, int u) {
+      constexpr int S = decltype(slot_c)::value;
+      if (u + 1 < nsteps) issue(ic<1 - S>(), u + 1);
+      compute(slot_c, u);
+      wait_vm0();
+      barrier_nofence();
+    };
+    for (int u = 0; u < nsteps; u += 2) {
+      step(ic<0>(), u);
+      if (u + 1 < nsteps) step(ic<1>(), u + 1);
+    }
+  }
+
+  // dK = scale * dK^T accumulated, dV; keys past the valid length get 0
+  if (j < p.Nk) {
+    const bool kv_ok = j < s.L;
+    uint16_t* dkr = p.dk + kv_base + (size_t)j * D;
+    uint16_t* dvr = p.dv + kv_base + (size_t)j * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int quad = 0; quad < 4; ++quad) {
+        f32x4 x, y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = kv_ok ? dka[db][4 * quad + e] * p.scale : 0.f;
+          y[e] = kv_ok ? dva[db][4 * quad + e] : 0.f;
+        }
+        const int col = db * 32 + quad * 8 + 4 * g;
+        *reinterpret_cast<bf16x4*>(dkr + col) =
+            __builtin_convertvector(x, bf16x4);
+        *reinterpret_cast<bf16x4*>(dvr + col) =
+            __builtin_convertvector(y, bf16x4);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
+    BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int QB = kWR * NW;  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[C::TILE];
+  auto kslot = [&](auto s) -> uint16_t* {
+    if constexpr (decltype(s)::value == 0) return Ks0; else return Ks1;
+  };
+  auto vslot = [&](auto s) -> uint16_t* {
+    if constexpr (decltype(s)::value == 0) return Vs0; else return Vs1;
+  };
+
+  // (batch, K/V head, query block, head of the group); causal blocks run
+  // heaviest (last rows) first
+  const int lid = xcd_block(blockIdx.x, p.total);
+  const int per_grp = p.G * p.nblk;
+  const int grp = lid / per_grp;
+  const int r0g = lid - grp * per_grp;
+  const int qrank = r0g / p.G;
+  const int hh = r0g - qrank * p.G;
+  const int qb = p.causal ? (p.nblk - 1 - qrank) : qrank;
+  const int b = grp / p.Hkv;
+  const int hk = grp - b * p.Hkv;
+  const int h = hk * p.G + hh;
+  const Seq s = seq_of(p, b);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ql = lane & 31;
+  const int g = lane >> 5;
+  const int q0 = qb * QB;
+  const int qw0 = q0 + wave * kWR;
+  const int qi = qw0 + ql;
+  const bool qlive = qi < s.Lq;
+  const RowKeys rk = keys_of_row(p, s, qlive, qi + s.off);
+
+  // the workgroup's tiles: sink tiles [0, ts1), then window tiles
+  // [tw0, tw1), merged into one run when they meet; step u visits tile_of(u)
+  const int rows_end = min(q0 + QB, s.Lq);
+  int nA = 0, tB0 = 0, nt = 0;
+  if (rows_end > q0) {
+    const RowKeys first = keys_of_row(p, s, true, q0 + s.off);
+    const RowKeys last = keys_of_row(p, s, true, rows_end - 1 + s.off);
+    int tw0 = first.lo / kRT, tw1 = (last.hw + kRT - 1) / kRT;
+    if (last.hw <= first.lo) tw0 = tw1 = 0;
+    const int ts1 = (last.sk + kRT - 1) / kRT;
+    if (ts1 >= tw0) {
+      nA = max(ts1, tw1);
+      nt = nA;
+    } else {
+      nA = ts1;
+      tB0 = tw0;
+      nt = ts1 + (tw1 - tw0);
+    }
+  }
+  auto tile_of = [&](int u) { return u < nA ? u : tB0 + (u - nA); };
+
+  // over the wave's live rows: hull and intersection of their key sets
+  const int wend = min(qw0 + kWR, s.Lq);
+  const bool wlive = wend > qw0;
+  RowKeys wf = {0, 0, 0, 0}, wl = {0, 0, 0, 0};
+  if (wlive) {
+    wf = keys_of_row(p, s, true, qw0 + s.off);
+    wl = keys_of_row(p, s, true, wend - 1 + s.off);
+  }
+  auto wave_needs = [&](int t) {
+    const int j0 = t * kRT;
+    return wlive && ((j0 < wl.hw && j0 + kRT > wf.lo) || j0 < wl.sk);
+  };
+  auto tile_full = [&](int t) {
+    const int j0 = t * kRT;
+    return (j0 >= wl.lo && j0 + kRT <= wf.hw) || j0 + kRT <= wf.sk;
+  };
+
+  // Q and dO of this lane's row as B operands; lse and delta of the row
+  const size_t bh = (size_t)b * p.Hq + h;
+  bf16x8 qf[C::KS], of[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (qlive) {
+      a = *reinterpret_cast<const u32x4*>(p.q + (bh * p.Nq + qi) * D +
+                                          16 * ks + 8 * g);
+      c = *reinterpret_cast<const u32x4*>(p.dout + (bh * p.Nq + qi) * D +
+                                          16 * ks + 8 * g);
+    }
+    qf[ks] = __builtin_bit_cast(bf16x8, a);
+    of[ks] = __builtin_bit_cast(bf16x8, c);
+  }
+  const float l2 = qlive ? p.lse2[bh * p.Nqp + qi] : INFINITY;
+  const float dl = qlive ? p.delta[bh * p.Nqp + qi] : 0.f;
+
+  f32x16 dqa[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
+
+  const int grp16 = lane >> 4;
+  const int i16 = lane & 15;
+  const int tr_off = (i16 >> 2) * C::STR + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  int arow[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+    arow[mb] = mfma_row(mb * 32 + ql) * C::STR + 8 * g;
+
+  const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
+  auto issue = [&](auto slot_c, int u) {
+    const int j0 = tile_of(u) * kRT;
+    const uint16_t* kb = p.k + kv_base + (size_t)j0 * D;
+    const uint16_t* vb = p.v + kv_base + (size_t)j0 * D;
+    auto ok = [&](int r) { return j0 + r < s.L; };
+    constexpr int NL = 2 * C::LOADS;
+#pragma unroll
+    for (int m = 0; m < (NL + NW - 1) / NW; ++m) {
+      const int u2 = wave + NW * m;
+      if (u2 < C::LOADS)
+        tile_load<D>(kb, kslot(slot_c), u2, lane, ok);
+      else if (u2 < NL)
+        tile_load<D>(vb, vslot(slot_c), u2 - C::LOADS, lane, ok);
+    }
+  };
+
+  auto compute = [&](auto slot_c, int u) {
+    const int t = tile_of(u);
+    if (!wave_needs(t)) return;
+    const uint16_t* Kt = kslot(slot_c);
+    const uint16_t* Vt = vslot(slot_c);
+    // S^T = K Q^T and dP^T = V dO^T: lane (query, g) holds keys
+    // mb*32 + 16g + r of the tile
+    f32x16 sa[2], pa[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sa[mb][r] = 0.f;
+        pa[mb][r] = 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Kt + arow[mb] + 16 * ks);
+        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sa[mb], 0,
+                                                         0, 0);
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Vt + arow[mb] + 16 * ks);
+        pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[ks], pa[mb], 0,
+                                                         0, 0);
+      }
+    const bool full = tile_full(t);
+    const int j0 = t * kRT;
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l2));
+        if (!full) {
+          const int jj = j0 + mb * 32 + 16 * g + r;
+          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
+            pr = 0.f;
+        }
+        dsv[r] = pr * (pa[mb][r] - dl);
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        f32x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = dsv[8 * m2 + e];
+        sb[mb][m2] = __builtin_convertvector(y, bf16x8);
+      }
+    }
+    // dQ^T += K^T dS^T over the tile's 64 keys
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int row0 = mb * 32 + 16 * g + 8 * m2;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 a = tr_read<C::STR>(Kt, tr_off, row0, db);
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
+                                                            dqa[db], 0, 0, 0);
+        }
+      }
+  };
+
+  if (nt > 0) {
+    issue(ic<0>(), 0);
+    wait_vm0();
+    barrier_nofence();
+    auto step = [&](auto slot_c, int u) {
+      constexpr int S = decltype(slot_c)::value;
+      if (u + 1 < nt) issue(ic<1 - S>(), u + 1);
+      compute(slot_c, u);
+      wait_vm0();
+      barrier_nofence();
+    };
+    for (int u = 0; u < nt; u += 2) {
+      step(ic<0>(), u);
+      if (u + 1 < nt) step(ic<1>(), u + 1);
+    }
+  }
+
+  // dQ = scale * dQ^T accumulated; dead rows get 0
+  if (qi < p.Nq) {
+    uint16_t* dqr = p.dq + (bh * p.Nq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int quad = 0; quad < 4; ++quad) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = qlive ? dqa[db][4 * quad + e] * p.scale : 0.f;
+        *reinterpret_cast<bf16x4*>(dqr + db * 32 + quad * 8 + 4 * g) =
+            __builtin_convertvector(x, bf16x4);
+      }
+  }
+}
+
+constexpr int kDkdvNW = 4;   // 128 keys per workgroup
+constexpr int kDqNW128 = 8;  // 256 rows per workgroup, two waves per SIMD
+constexpr int kDqNW64 = 4;
+
+template <int D, int NWK, int NWQ>
+hipError_t launch_all(BwdParams p, hipStream_t st) {
+  const long long rows = (long long)p.B * p.Hq * p.Nqp;
+  const long long waves = (rows * D / 8 + 63) / 64;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((waves + 3) / 4)),
+                     dim3(256), 0, st, p);
+  BwdParams a = p;
+  a.nblk = (p.Nk + kWR * NWK - 1) / (kWR * NWK);
+  a.total = p.B * p.Hkv * a.nblk;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK>), dim3(a.total),
+                     dim3(64 * NWK), 0, st, a);
+  BwdParams c = p;
+  c.nblk = (p.Nq + kWR * NWQ - 1) / (kWR * NWQ);
+  c.total = p.B * p.Hq * c.nblk;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3(c.total), dim3(64 * NWQ),
+                     0, st, c);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const Problem& pr) {
+  const size_t nqp = (size_t)((pr.Nq + kRT - 1) / kRT) * kRT;
+  return 2 * (size_t)pr.B * pr.Hq * nqp * sizeof(float);
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse,
+                           void* dq, void* dk, void* dv, const Problem& pr,
+                           void* ws, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.seqlens = pr.seqlens;
+  p.B = pr.B;
+  p.Hq = pr.Hq;
+  p.Hkv = pr.Hkv;
+  p.Nq = pr.Nq;
+  p.Nk = pr.Nk;
+  p.Nqp = (pr.Nq + kRT - 1) / kRT * kRT;
+  p.G = pr.Hq / pr.Hkv;
+  p.causal = pr.causal;
+  p.window = pr.window;
+  p.window_right = pr.window_right;
+  p.sinks = pr.sinks;
+  p.scale = pr.scale;
+  p.c = pr.scale * 1.4426950408889634f;
+  const size_t n = (size_t)pr.B * pr.Hq * p.Nqp;
+  p.lse2 = static_cast<float*>(ws);
+  p.delta = p.lse2 + n;
+  p.nblk = 0;
+  p.total = 0;
+  if (pr.d == 128) return launch_all<128, kDkdvNW, kDqNW128>(p, stream);
+  return launch_all<64, kDkdvNW, kDqNW64>(p, stream);
+}
+
+}  // namespace miattn

@@ -32,6 +32,14 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
                               void* o, float* lse, const Problem& p, void* ws,
                               hipStream_t stream);
 
+// bf16 backward: dQ, dK, dV from q, k, v, o, dO and the forward lse.  `ws`
+// must hold bwd_workspace_bytes(p) bytes.
+size_t bwd_workspace_bytes(const Problem& p);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v,
+                           const void* o, const void* dout, const float* lse,
+                           void* dq, void* dk, void* dv, const Problem& p,
+                           void* ws, hipStream_t stream);
+
 // fp32 path (any Nq in {1, Nk}).
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v,
                            float* o, float* lse, const Problem& p,
