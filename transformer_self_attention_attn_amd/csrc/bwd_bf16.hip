@@ -37,7 +37,14 @@
 // Tiles arrive by 16-byte direct-to-LDS loads into two ring slots per
 // operand, each slot its own LDS object named by a compile-time index; rows
 // past the valid length (or dead query rows) read a block of zeros, so padded
-// contents never enter a product.
+// contents never enter a product.  A tile is read two ways: row-wise (16
+// bytes per lane, the A operand of Q K^T) and column-wise (the transposing
+// read, the A operand of dO^T P); tiles are stored unpadded with the 16-byte
+// chunks of each row permuted by an XOR of row bits (see swz), which keeps
+// both kinds of read free of LDS bank conflicts.
+// The dK/dV step runs its 64 MFMAs (d=128) from a ring of operands read four
+// MFMAs ahead, and the softmax of one 32-row half of the tile runs between
+// the MFMAs of the other half.
 #include "kernels.h"
 
 #include <cmath>
@@ -88,14 +95,35 @@ struct BwdParams {
 
 template <int D>
 struct BCfg {
-  static constexpr int STR = D + 8;           // tile row stride (elements)
-  static constexpr int CH = STR / 8;          // 16-byte chunks per tile row
-  static constexpr int TILE = kRT * STR;      // elements per tile
+  static constexpr int CH = D / 8;            // 16-byte chunks per tile row
+  static constexpr int TILE = kRT * D;        // elements per tile (unpadded)
   static constexpr int LOADS = kRT * CH / 64; // wave-wide 1 KB loads per tile
   static constexpr int KS = D / 16;           // k-steps of a D-long product
   static constexpr int DB = D / 32;           // 32-row blocks of a D^T result
   static_assert(kRT * CH % 64 == 0, "tile loads");
 };
+
+// Chunk permutation of a tile row: logical 16-byte chunk c of row r sits at
+// chunk c ^ swz(r).  A row-wise operand read has 16 lanes read one chunk of
+// 16 different rows (rows mfma_row(0..15) and the like), a transposing read
+// has 32 lanes read chunks 4m .. 4m+3 of 4 consecutive rows; with this XOR
+// each such group covers the 64 four-byte LDS banks once (d=128: one row per
+// 256-byte bank line; d=64: two).
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+  else
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>());
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Valid length and row positions of batch b: rows i < Lq are live and row i
 // sits at position i + off (Nq == Nk: the first L rows; otherwise the last Nq
@@ -185,40 +213,59 @@ __device__ inline int xcd_block(int bid, int n) {
   return xcd * per + min(xcd, rem) + slot;
 }
 
-// One wave-wide direct-to-LDS load of a [64][STR] tile: wave load i fills
-// tile bytes [i*1024, +1024); lane l writes 16-byte chunk i*64 + l, i.e.
-// (row r, chunk c) of the padded row.  `row_ok(r)` false -> zeros; pad chunks
-// take the row's first chunk (they are never read).
+// One wave-wide direct-to-LDS load of a [64][D] tile: wave load i fills
+// tile bytes [i*1024, +1024); lane l writes 16-byte slot s = i*64 + l, which
+// is physical chunk s % CH of row s / CH and so holds that row's logical
+// chunk (s % CH) ^ swz(row).  `row_ok(r)` false -> zeros.
 template <int D, typename RowOk>
 __device__ inline void tile_load(const uint16_t* base, uint16_t* tile, int i,
                                  int lane, RowOk row_ok) {
   using C = BCfg<D>;
   const int s = i * 64 + lane;
   const int r = s / C::CH;
-  const int c = s - r * C::CH;
-  const void* src = row_ok(r) ? (const void*)(base + (size_t)r * D +
-                                              (c < D / 8 ? c * 8 : 0))
+  const int c = (s % C::CH) ^ swz<D>(r);
+  const void* src = row_ok(r) ? (const void*)(base + (size_t)r * D + c * 8)
                               : (const void*)kZeroBwd;
   __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + i * 512), 16, 0,
                                    0);
 }
 
-// A operand of X^T (X a [64][STR] tile in LDS): for the 32 columns
-// db*32 .. +31 (one per lane mod 32) the 8 tile rows row0 .. row0+3 and
-// row0+4 .. row0+7 of this lane's half, read with the transposing LDS read.
-template <int STR>
-__device__ inline bf16x8 tr_read(const uint16_t* tile, int lane_off, int row0,
-                                 int db) {
-  bf16x8 a;
+// Element offset of this lane's row-wise A-operand piece: tile row
+// mfma_row(32 mb + lane % 32), columns 16 ks + 8 g .. +7 (g = lane / 32).
+template <int D>
+__device__ inline int a_off(int lane, int mb, int ks) {
+  const int row = mfma_row(mb * 32 + (lane & 31));
+  return row * D + 8 * ((2 * ks + (lane >> 5)) ^ swz<D>(row));
+}
+
+// Element offset of this lane's 8-byte piece of a transposing read of tile
+// rows R .. R+3, R = 32 mb + 16 g + 8 m2 + 4 half, columns 32 db .. +31,
+// less the part (32 mb + 8 m2 + 4 half) * D that is a compile-time constant
+// at every use.  Lane i of each 16-lane group addresses row R + i / 4,
+// columns 32 db + 16 (lane / 16 % 2) + 4 (i % 4) .. +3; with R % 4 == 0 the
+// chunk permutation of that row is fj + half + 2 g.
+template <int D>
+__device__ inline int tr_off(int lane, int half, int db) {
+  const int g = lane >> 5, grp16 = lane >> 4, i16 = lane & 15;
+  const int j = i16 >> 2;
+  const int fj = (D == 128) ? 4 * j : 4 * ((j >> 1) & 1);
+  const int lb = 2 * (grp16 & 1) + ((i16 & 3) >> 1);
+  const int pc = 4 * (db ^ (fj >> 2)) + (lb ^ (half + 2 * g));
+  return (16 * g + j) * D + 8 * pc + 4 * (i16 & 1);
+}
+
+// A operand of X^T for the lane's k-group: rows R .. R+7 (two transposing
+// reads of four rows), columns 32 db .. +31; off = tr_off(lane, 0/1, db).
+__device__ inline bf16x8 tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  bf16x8 r;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const uint16_t* ptr = tile + lane_off + (row0 + 4 * half) * STR + db * 32;
-    const i16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      a[4 * half + e] = __builtin_bit_cast(__bf16, (short)r4[e]);
+  for (int e = 0; e < 4; ++e) {
+    r[e] = __builtin_bit_cast(__bf16, (short)a[e]);
+    r[4 + e] = __builtin_bit_cast(__bf16, (short)b[e]);
   }
-  return a;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -367,14 +414,17 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       dva[db][r] = 0.f;
     }
 
-  // lane offsets of the LDS operand reads
-  const int grp16 = lane >> 4;
-  const int i16 = lane & 15;
-  const int tr_off = (i16 >> 2) * C::STR + 16 * (grp16 & 1) + 4 * (i16 & 3);
-  int arow[2];
+  // lane offsets of the LDS operand reads (the same for the Q and dO tiles)
+  int aoff[2][C::KS];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
-    arow[mb] = mfma_row(mb * 32 + kl) * C::STR + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) aoff[mb][ks] = a_off<D>(lane, mb, ks);
+  int toff[2][C::DB];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
 
   // loads of step u (query head hk*G + u / nt, tile t0 + u % nt) into slot S
   auto issue = [&](auto slot_c, int u) {
@@ -403,6 +453,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     }
   };
 
+  // One step, as a sequence of NM MFMAs:
+  //   [0, NA)         S = Q K^T and dP = dO V^T of tile rows 0 .. 31
+  //   [NA, 2NA)       the same for rows 32 .. 63, with P and dS of rows
+  //                   0 .. 31 computed in between
+  //   [2NA, 2NA+NB)   dV^T += dO^T P and dK^T += Q^T dS over rows 0 .. 31,
+  //                   with P and dS of rows 32 .. 63 in between
+  //   [2NA+NB, NM)    the same over rows 32 .. 63
+  // Each MFMA's A operand is read from LDS four MFMAs ahead.
+  constexpr int NA = 2 * C::KS;
+  constexpr int NB = 4 * C::DB;
+  constexpr int NM = 2 * NA + 2 * NB;
+  constexpr int AHEAD = 4;
+  constexpr int RING = AHEAD + 1;
+  constexpr int EPS = 16 / NA;  // softmax elements per MFMA slot
+  static_assert(NA == NB && 16 % NA == 0, "slots");
+
   auto compute = [&](auto slot_c, int u) {
     const int t = t0 + u % nt;
     if (!wave_needs(t)) return;
@@ -410,41 +476,63 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     const uint16_t* Ot = oslot(slot_c);
     const float* Lt = lslot(slot_c);
     const float* Dt = dslot(slot_c);
-    // S = Q K^T and dP = dO V^T: lane (key, g) holds tile rows
-    // mb*32 + 16g + r
+
+    auto fetch = [&](auto i_c) -> bf16x8 {
+      constexpr int i = decltype(i_c)::value;
+      if constexpr (i < 2 * NA) {
+        constexpr int mb = i / NA, ks = (i % NA) / 2;
+        const uint16_t* tb = (i % 2 == 0) ? Qt : Ot;
+        return *reinterpret_cast<const bf16x8*>(tb + aoff[mb][ks]);
+      } else {
+        constexpr int x = i - 2 * NA;
+        constexpr int mb = x / NB, r = x % NB;
+        constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+        const uint16_t* tb = (r % 2 == 0) ? Ot : Qt;
+        constexpr int c0 = (32 * mb + 8 * m2) * D;
+        return tr_pair(tb + toff[0][db] + c0, tb + toff[1][db] + c0 + 4 * D);
+      }
+    };
+
     f32x16 sa[2], pa[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sa[mb][r] = 0.f;
-        pa[mb][r] = 0.f;
+    bf16x8 pb[2][2], sb[2][2];
+    const f32x16 zero = {};
+    auto mfma = [&](auto i_c, const bf16x8& a) {
+      constexpr int i = decltype(i_c)::value;
+      if constexpr (i < 2 * NA) {
+        constexpr int mb = i / NA, ks = (i % NA) / 2;
+        if constexpr (i % 2 == 0)
+          sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, kf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0);
+        else
+          pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, vf[ks], ks == 0 ? zero : pa[mb], 0, 0, 0);
+      } else {
+        constexpr int x = i - 2 * NA;
+        constexpr int mb = x / NB, r = x % NB;
+        constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+        if constexpr (r % 2 == 0)
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][m2],
+                                                            dva[db], 0, 0, 0);
+        else
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
+                                                            dka[db], 0, 0, 0);
       }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Qt + arow[mb] + 16 * ks);
-        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sa[mb], 0,
-                                                         0, 0);
-      }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Ot + arow[mb] + 16 * ks);
-        pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], pa[mb], 0,
-                                                         0, 0);
-      }
-    // P and dS; rows outside this key's range are masked (partial tiles)
+    };
+
+    // softmax of rows 32 mb + 16 g + r of this tile (lane = key): a row
+    // outside [rlo, rhi) is masked unless the tile is full
     const bool full = tile_full(t);
     const int r0 = t * kRT;
-    bf16x8 pb[2][2], sb[2][2];
+    float lsv[16], dlv[16], pvv[16], dsv[16];
+    int mlo[2], mhi[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      float pv[16], dsv[16];
+      const int base = r0 + mb * 32 + 16 * g;
+      mlo[mb] = full ? -1 : rlo - base;
+      mhi[mb] = full ? 16 : rhi - base;
+    }
+    auto stats = [&](auto mb_c) {
+      constexpr int mb = decltype(mb_c)::value;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 l4 =
@@ -453,48 +541,55 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
             *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l4[e]));
-          if (!full) {
-            const int i = r0 + mb * 32 + 16 * g + r;
-            if (i < rlo || i >= rhi) pr = 0.f;
-          }
-          pv[r] = pr;
-          dsv[r] = pr * (pa[mb][r] - d4[e]);
+          lsv[4 * q4 + e] = l4[e];
+          dlv[4 * q4 + e] = d4[e];
         }
       }
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
+    };
+    auto element = [&](auto mb_c, auto r_c) {
+      constexpr int mb = decltype(mb_c)::value, r = decltype(r_c)::value;
+      float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -lsv[r]));
+      pr = (r >= mlo[mb] && r < mhi[mb]) ? pr : 0.f;
+      pvv[r] = pr;
+      dsv[r] = pr * (pa[mb][r] - dlv[r]);
+      if constexpr (r % 8 == 7) {
+        constexpr int m2 = r / 8;
         f32x8 x, y;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = pv[8 * m2 + e];
+          x[e] = pvv[8 * m2 + e];
           y[e] = dsv[8 * m2 + e];
         }
         pb[mb][m2] = __builtin_convertvector(x, bf16x8);
         sb[mb][m2] = __builtin_convertvector(y, bf16x8);
       }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        const int row0 = mb * 32 + 16 * g + 8 * m2;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a = tr_read<C::STR>(Ot, tr_off, row0, db);
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][m2],
-                                                            dva[db], 0, 0, 0);
-        }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a = tr_read<C::STR>(Qt, tr_off, row0, db);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
-                                                            dka[db], 0, 0, 0);
-        }
+    };
+
+    bf16x8 ring[RING];
+    static_for<0, AHEAD>([&](auto i_c) {
+      ring[decltype(i_c)::value] = fetch(i_c);
+    });
+    static_for<0, NM>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      if constexpr (i + AHEAD < NM)
+        ring[(i + AHEAD) % RING] = fetch(ic<i + AHEAD>());
+      mfma(i_c, ring[i % RING]);
+      // softmax of rows 0 .. 31 during slots [NA, 2NA), of rows 32 .. 63
+      // during [2NA, 2NA+NB)
+      if constexpr (i >= NA && i < 2 * NA + NB) {
+        constexpr int mbs = (i < 2 * NA) ? 0 : 1;
+        constexpr int k = (i < 2 * NA) ? i - NA : i - 2 * NA;
+        if constexpr (k == 0) stats(ic<mbs>());
+        static_for<0, EPS>([&](auto e_c) {
+          element(ic<mbs>(), ic<k * EPS + decltype(e_c)::value>());
+        });
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    });
   };
+
 
   if (nsteps > 0) {
     issue(ic<0>(), 0);
@@ -643,13 +738,16 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
 
-  const int grp16 = lane >> 4;
-  const int i16 = lane & 15;
-  const int tr_off = (i16 >> 2) * C::STR + 16 * (grp16 & 1) + 4 * (i16 & 3);
-  int arow[2];
+  int aoff[2][C::KS];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
-    arow[mb] = mfma_row(mb * 32 + ql) * C::STR + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) aoff[mb][ks] = a_off<D>(lane, mb, ks);
+  int toff[2][C::DB];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
   auto issue = [&](auto slot_c, int u) {
@@ -688,7 +786,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Kt + arow[mb] + 16 * ks);
+            *reinterpret_cast<const bf16x8*>(Kt + aoff[mb][ks]);
         sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sa[mb], 0,
                                                          0, 0);
       }
@@ -697,7 +795,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Vt + arow[mb] + 16 * ks);
+            *reinterpret_cast<const bf16x8*>(Vt + aoff[mb][ks]);
         pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[ks], pa[mb], 0,
                                                          0, 0);
       }
@@ -730,10 +828,11 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) {
-        const int row0 = mb * 32 + 16 * g + 8 * m2;
+        const int c0 = (32 * mb + 8 * m2) * D;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a = tr_read<C::STR>(Kt, tr_off, row0, db);
+          const bf16x8 a =
+              tr_pair(Kt + toff[0][db] + c0, Kt + toff[1][db] + c0 + 4 * D);
           dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
                                                             dqa[db], 0, 0, 0);
         }
