@@ -34,10 +34,11 @@
 //               S^T = K Q^T  and  dP^T = V dO^T
 //               dS^T in registers (lane = query, 16 consecutive keys)
 //               dQ^T += K^T dS^T   (A = transposing LDS reads of K)
-// Tiles arrive by 16-byte direct-to-LDS loads into two ring slots per
-// operand, each slot its own LDS object named by a compile-time index; rows
-// past the valid length (or dead query rows) read a block of zeros, so padded
-// contents never enter a product.  A tile is read two ways: row-wise (16
+// Tiles arrive by 16-byte direct-to-LDS buffer loads into ring slots (three
+// in bwd_dkdv, two in bwd_dq), each slot its own LDS object named by a
+// compile-time index; rows past the valid length (or dead query rows) lie
+// outside the buffer resource and read zeros, so padded contents never enter
+// a product.  A tile is read two ways: row-wise (16
 // bytes per lane, the A operand of Q K^T) and column-wise (the transposing
 // read, the A operand of dO^T P); tiles are stored unpadded with the 16-byte
 // chunks of each row permuted by an XOR of row bits (see swz), which keeps
@@ -50,8 +51,19 @@
 #include <cmath>
 #include <type_traits>
 
+typedef int bwd_i32x4 __attribute__((ext_vector_type(4)));
+
+// The direct-to-LDS buffer load (buffer_load_dword* ... lds), declared by
+// its intrinsic name with the resource as four plain ints: written with the
+// resource-type builtins, these kernels lost their host-side launch stubs
+// in this compiler.
+__device__ void miattn_buffer_load_lds(
+    bwd_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+    int voffset, int soffset, int offset,
+    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace miattn {
-namespace {
+namespace bwd_impl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -70,9 +82,6 @@ constexpr int kRT = 64;    // rows of a streamed tile (queries or keys)
 constexpr int kWR = 32;    // rows a wave owns (keys in dK/dV, queries in dQ)
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies
 constexpr int kBig = 1 << 30;
-
-__device__ __attribute__((aligned(16))) const unsigned kZeroBwd[4] = {0u, 0u,
-                                                                      0u, 0u};
 
 struct BwdParams {
   const uint16_t* q;
@@ -186,6 +195,23 @@ __device__ inline int mfma_row(int m) {
 }
 
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// Waits until at most n (0 .. 15, wave-uniform) vector-memory loads of this
+// wave are outstanding; other counters untouched (vmcnt is bits 3:0 here).
+__device__ inline void wait_vmcnt_rt(int n) {
+  switch (n) {
+#define MIATTN_BW(N) \
+  case N:            \
+    __builtin_amdgcn_s_waitcnt(0xF70 | (N)); \
+    break;
+    MIATTN_BW(1) MIATTN_BW(2) MIATTN_BW(3) MIATTN_BW(4) MIATTN_BW(5)
+    MIATTN_BW(6) MIATTN_BW(7) MIATTN_BW(8) MIATTN_BW(9) MIATTN_BW(10)
+    MIATTN_BW(11) MIATTN_BW(12) MIATTN_BW(13) MIATTN_BW(14) MIATTN_BW(15)
+#undef MIATTN_BW
+    default:
+      __builtin_amdgcn_s_waitcnt(0xF70);
+  }
+}
 __device__ inline void barrier_nofence() {
   asm volatile("s_barrier" ::: "memory");
 }
@@ -216,18 +242,31 @@ __device__ inline int xcd_block(int bid, int n) {
 // One wave-wide direct-to-LDS load of a [64][D] tile: wave load i fills
 // tile bytes [i*1024, +1024); lane l writes 16-byte slot s = i*64 + l, which
 // is physical chunk s % CH of row s / CH and so holds that row's logical
-// chunk (s % CH) ^ swz(row).  `row_ok(r)` false -> zeros.
-template <int D, typename RowOk>
-__device__ inline void tile_load(const uint16_t* base, uint16_t* tile, int i,
-                                 int lane, RowOk row_ok) {
+// chunk (s % CH) ^ swz(row).  Loads go through a buffer resource whose size
+// ends at the last valid row, with the whole offset in the per-lane operand,
+// so a row past the valid length reads zeros.
+// Byte offset, within a [64][D] tile, of the source of this lane's part of
+// wave load i: row s / CH, logical chunk (s % CH) ^ swz(row).
+template <int D>
+__device__ inline unsigned tile_src_off(int i, int lane) {
   using C = BCfg<D>;
   const int s = i * 64 + lane;
   const int r = s / C::CH;
   const int c = (s % C::CH) ^ swz<D>(r);
-  const void* src = row_ok(r) ? (const void*)(base + (size_t)r * D + c * 8)
-                              : (const void*)kZeroBwd;
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + i * 512), 16, 0,
-                                   0);
+  return (unsigned)((r * D + c * 8) * 2);
+}
+
+// Buffer resource over `bytes` bytes at `base` (stride 0, 32-bit data
+// format): a load at or past the end reads zeros, which is how rows past the
+// valid length enter LDS as zeros.
+__device__ inline bwd_i32x4 rows_rsrc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  bwd_i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
 // Element offset of this lane's row-wise A-operand piece: tile row
@@ -315,25 +354,38 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     BwdParams p) {
   using C = BCfg<D>;
   constexpr int KB = kWR * NW;  // keys per workgroup
+  // three ring slots of (Q tile, dO tile, lse, delta)
   __shared__ __attribute__((aligned(16))) uint16_t Qs0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t Qs1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs2[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t Os0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t Os1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Os2[C::TILE];
   __shared__ __attribute__((aligned(16))) float Ls0[kRT];
   __shared__ __attribute__((aligned(16))) float Ls1[kRT];
+  __shared__ __attribute__((aligned(16))) float Ls2[kRT];
   __shared__ __attribute__((aligned(16))) float Ds0[kRT];
   __shared__ __attribute__((aligned(16))) float Ds1[kRT];
+  __shared__ __attribute__((aligned(16))) float Ds2[kRT];
   auto qslot = [&](auto s) -> uint16_t* {
-    if constexpr (decltype(s)::value == 0) return Qs0; else return Qs1;
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return Qs0; else if constexpr (S == 1) return Qs1;
+    else return Qs2;
   };
   auto oslot = [&](auto s) -> uint16_t* {
-    if constexpr (decltype(s)::value == 0) return Os0; else return Os1;
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return Os0; else if constexpr (S == 1) return Os1;
+    else return Os2;
   };
   auto lslot = [&](auto s) -> float* {
-    if constexpr (decltype(s)::value == 0) return Ls0; else return Ls1;
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return Ls0; else if constexpr (S == 1) return Ls1;
+    else return Ls2;
   };
   auto dslot = [&](auto s) -> float* {
-    if constexpr (decltype(s)::value == 0) return Ds0; else return Ds1;
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return Ds0; else if constexpr (S == 1) return Ds1;
+    else return Ds2;
   };
 
   // (batch, K/V head, key block), key blocks of one group adjacent; within a
@@ -378,7 +430,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       nt = (hi + kRT - 1) / kRT - t0;
     }
   }
-  const int nsteps = nt * p.G;  // (query head, tile) pairs
+  // (tile, query head) pairs, tile-major from the last tile down: every key
+  // block of a group starts at the same tile and walks the same tiles in the
+  // same order, so the blocks running together share each tile in L2
+  const int nsteps = nt * p.G;
+  const int t_last = t0 + nt - 1;
   auto wave_needs = [&](int t) {
     const int r0 = t * kRT;
     return r0 < w_hi_max && r0 + kRT > w_lo_min;
@@ -427,28 +483,46 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
 
   // loads of step u (query head hk*G + u / nt, tile t0 + u % nt) into slot S
+  // this wave's loads of a step: wave load u2 = wave + NW*m; u2 < LOADS is
+  // a Q tile load, then dO tile loads, then lse and delta (64 floats each);
+  // per-lane source offsets within a tile are the same every step
+  constexpr int NL = 2 * C::LOADS + 2;
+  constexpr int LW = (NL + NW - 1) / NW;
+  unsigned toffs[LW];
+#pragma unroll
+  for (int m = 0; m < LW; ++m) {
+    const int u2 = wave + NW * m;
+    toffs[m] = u2 < C::LOADS       ? tile_src_off<D>(u2, lane)
+               : u2 < 2 * C::LOADS ? tile_src_off<D>(u2 - C::LOADS, lane)
+                                   : (unsigned)(lane * 4);
+  }
+  const int qbytes = s.Lq * D * 2;  // rows past the live rows read zeros
   auto issue = [&](auto slot_c, int u) {
-    const int h = hk * p.G + u / nt;
-    const int t = t0 + u % nt;
+    const int h = hk * p.G + u % p.G;
+    const int t = t_last - u / p.G;
     const int r0 = t * kRT;
     const size_t bh = (size_t)b * p.Hq + h;
-    const uint16_t* qb = p.q + (bh * p.Nq + r0) * D;
-    const uint16_t* ob = p.dout + (bh * p.Nq + r0) * D;
-    auto ok = [&](int r) { return r0 + r < s.Lq; };
-    constexpr int NL = 2 * C::LOADS + 2;
+    const auto qrs = rows_rsrc(p.q + bh * p.Nq * D, qbytes);
+    const auto ors = rows_rsrc(p.dout + bh * p.Nq * D, qbytes);
+    const int tb = r0 * D * 2;
 #pragma unroll
-    for (int m = 0; m < (NL + NW - 1) / NW; ++m) {
+    for (int m = 0; m < LW; ++m) {
       const int u2 = wave + NW * m;
       if (u2 < C::LOADS) {
-        tile_load<D>(qb, qslot(slot_c), u2, lane, ok);
+        miattn_buffer_load_lds(
+            qrs, (lds_void*)(qslot(slot_c) + u2 * 512), 16, toffs[m] + tb, 0,
+            0, 0);
       } else if (u2 < 2 * C::LOADS) {
-        tile_load<D>(ob, oslot(slot_c), u2 - C::LOADS, lane, ok);
-      } else if (u2 == 2 * C::LOADS) {
-        __builtin_amdgcn_global_load_lds(p.lse2 + bh * p.Nqp + r0 + lane,
-                                         (lds_void*)lslot(slot_c), 4, 0, 0);
-      } else if (u2 == 2 * C::LOADS + 1) {
-        __builtin_amdgcn_global_load_lds(p.delta + bh * p.Nqp + r0 + lane,
-                                         (lds_void*)dslot(slot_c), 4, 0, 0);
+        miattn_buffer_load_lds(
+            ors, (lds_void*)(oslot(slot_c) + (u2 - C::LOADS) * 512), 16,
+            toffs[m] + tb, 0, 0, 0);
+      } else if (u2 < NL) {
+        const bool isl = u2 == 2 * C::LOADS;
+        const auto rs =
+            rows_rsrc((isl ? p.lse2 : p.delta) + bh * p.Nqp, p.Nqp * 4);
+        miattn_buffer_load_lds(
+            rs, (lds_void*)(isl ? lslot(slot_c) : dslot(slot_c)), 4,
+            toffs[m] + r0 * 4, 0, 0, 0);
       }
     }
   };
@@ -470,7 +544,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   static_assert(NA == NB && 16 % NA == 0, "slots");
 
   auto compute = [&](auto slot_c, int u) {
-    const int t = t0 + u % nt;
+    const int t = t_last - u / p.G;
     if (!wave_needs(t)) return;
     const uint16_t* Qt = qslot(slot_c);
     const uint16_t* Ot = oslot(slot_c);
@@ -591,20 +665,34 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   };
 
 
+  // step u computes from slot u % 3 while the loads of step u + 2 fill slot
+  // (u + 2) % 3; before the barrier that ends step u each wave waits for its
+  // loads of step u + 1 (all but the nl loads it issued for step u + 2)
+  const int nl = (NL - wave + NW - 1) / NW;  // loads per step of this wave
   if (nsteps > 0) {
     issue(ic<0>(), 0);
-    wait_vm0();
+    if (1 < nsteps) {
+      issue(ic<1>(), 1);
+      wait_vmcnt_rt(nl);
+    } else {
+      wait_vm0();
+    }
     barrier_nofence();
     auto step = [&](auto slot_c, int u) {
       constexpr int S = decltype(slot_c)::value;
-      if (u + 1 < nsteps) issue(ic<1 - S>(), u + 1);
+      const bool more = u + 2 < nsteps;
+      if (more) issue(ic<(S + 2) % 3>(), u + 2);
       compute(slot_c, u);
-      wait_vm0();
+      if (more)
+        wait_vmcnt_rt(nl);
+      else
+        wait_vm0();
       barrier_nofence();
     };
-    for (int u = 0; u < nsteps; u += 2) {
+    for (int u = 0; u < nsteps; u += 3) {
       step(ic<0>(), u);
       if (u + 1 < nsteps) step(ic<1>(), u + 1);
+      if (u + 2 < nsteps) step(ic<2>(), u + 2);
     }
   }
 
@@ -750,19 +838,30 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
     for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
-  auto issue = [&](auto slot_c, int u) {
-    const int j0 = tile_of(u) * kRT;
-    const uint16_t* kb = p.k + kv_base + (size_t)j0 * D;
-    const uint16_t* vb = p.v + kv_base + (size_t)j0 * D;
-    auto ok = [&](int r) { return j0 + r < s.L; };
-    constexpr int NL = 2 * C::LOADS;
+  // this wave's tile loads: wave load u2 = wave + NW*m, K tile loads first
+  constexpr int NL = 2 * C::LOADS;
+  constexpr int LW = (NL + NW - 1) / NW;
+  unsigned toffs[LW];
 #pragma unroll
-    for (int m = 0; m < (NL + NW - 1) / NW; ++m) {
+  for (int m = 0; m < LW; ++m) {
+    const int u2 = wave + NW * m;
+    toffs[m] = tile_src_off<D>(u2 < C::LOADS ? u2 : u2 - C::LOADS, lane);
+  }
+  const auto krs = rows_rsrc(p.k + kv_base, s.L * D * 2);
+  const auto vrs = rows_rsrc(p.v + kv_base, s.L * D * 2);
+  auto issue = [&](auto slot_c, int u) {
+    const int tb = tile_of(u) * kRT * D * 2;
+#pragma unroll
+    for (int m = 0; m < LW; ++m) {
       const int u2 = wave + NW * m;
       if (u2 < C::LOADS)
-        tile_load<D>(kb, kslot(slot_c), u2, lane, ok);
+        miattn_buffer_load_lds(
+            krs, (lds_void*)(kslot(slot_c) + u2 * 512), 16, toffs[m] + tb, 0,
+            0, 0);
       else if (u2 < NL)
-        tile_load<D>(vb, vslot(slot_c), u2 - C::LOADS, lane, ok);
+        miattn_buffer_load_lds(
+            vrs, (lds_void*)(vslot(slot_c) + (u2 - C::LOADS) * 512), 16,
+            toffs[m] + tb, 0, 0, 0);
     }
   };
 
@@ -896,7 +995,9 @@ hipError_t launch_all(BwdParams p, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace bwd_impl
+
+using namespace bwd_impl;
 
 size_t bwd_workspace_bytes(const Problem& pr) {
   const size_t nqp = (size_t)((pr.Nq + kRT - 1) / kRT) * kRT;
