@@ -15,8 +15,8 @@
 // kernels.
 //
 // Three launches, no atomics (results do not depend on scheduling):
-//   bwd_pre   delta_i from dO and O, and lse_i * log2(e), per query row, into
-//             a workspace padded to 64 rows; a row that sees no key gets
+//   bwd_pre   -delta_i from dO and O, and lse_i * log2(e), per query row,
+//             into a workspace padded to 64 rows; a row that sees no key gets
 //             +inf, so every probability of it is exactly 0.
 //   bwd_dkdv  one workgroup per (batch, K/V head, block of 32*NW keys); wave
 //             w owns 32 keys and holds their K and V as MFMA B operands in
@@ -94,7 +94,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* lse2;   // [B*Hq][Nqp]: lse * log2(e); +inf on rows that see no key
-  float* delta;  // [B*Hq][Nqp]: dO . O; 0 on those rows
+  float* delta;  // [B*Hq][Nqp]: -(dO . O); 0 on those rows
   const int* seqlens;
   int B, Hq, Hkv, Nq, Nk, Nqp, G, causal, window, window_right, sinks;
   int nblk, total;  // blocks per (batch, head) and in the grid
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 #pragma unroll
   for (int x = 1; x < LPR; x <<= 1) acc += __shfl_xor(acc, x);
   if (valid && lane % LPR == 0) {
-    p.delta[row] = live ? acc : 0.f;
+    p.delta[row] = live ? -acc : 0.f;
     p.lse2[row] = live ? lse * 1.4426950408889634f : INFINITY;
   }
 }
@@ -543,9 +543,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   constexpr int EPS = 16 / NA;  // softmax elements per MFMA slot
   static_assert(NA == NB && 16 % NA == 0, "slots");
 
-  auto compute = [&](auto slot_c, int u) {
-    const int t = t_last - u / p.G;
-    if (!wave_needs(t)) return;
+  // FULL: every (row, key) pair of the tile is allowed, no mask arithmetic
+  auto compute_t = [&](auto slot_c, auto full_c, int t) {
+    constexpr bool FULL = decltype(full_c)::value;
     const uint16_t* Qt = qslot(slot_c);
     const uint16_t* Ot = oslot(slot_c);
     const float* Lt = lslot(slot_c);
@@ -570,6 +570,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     f32x16 sa[2], pa[2];
     bf16x8 pb[2][2], sb[2][2];
     const f32x16 zero = {};
+    // dP starts from -delta of its rows, so the accumulator ends at
+    // dP - delta (the factor of dS besides P)
+    f32x16 nd0[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 d4 =
+            *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nd0[mb][4 * q4 + e] = d4[e];
+      }
     auto mfma = [&](auto i_c, const bf16x8& a) {
       constexpr int i = decltype(i_c)::value;
       if constexpr (i < 2 * NA) {
@@ -579,7 +591,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
               a, kf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0);
         else
           pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, vf[ks], ks == 0 ? zero : pa[mb], 0, 0, 0);
+              a, vf[ks], ks == 0 ? nd0[mb] : pa[mb], 0, 0, 0);
       } else {
         constexpr int x = i - 2 * NA;
         constexpr int mb = x / NB, r = x % NB;
@@ -595,37 +607,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
 
     // softmax of rows 32 mb + 16 g + r of this tile (lane = key): a row
     // outside [rlo, rhi) is masked unless the tile is full
-    const bool full = tile_full(t);
     const int r0 = t * kRT;
-    float lsv[16], dlv[16], pvv[16], dsv[16];
+    float pvv[16], dsv[16];
+    f32x4 l4;
     int mlo[2], mhi[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int base = r0 + mb * 32 + 16 * g;
-      mlo[mb] = full ? -1 : rlo - base;
-      mhi[mb] = full ? 16 : rhi - base;
+      mlo[mb] = rlo - base;
+      mhi[mb] = rhi - base;
     }
-    auto stats = [&](auto mb_c) {
-      constexpr int mb = decltype(mb_c)::value;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 =
-            *reinterpret_cast<const f32x4*>(Lt + mb * 32 + 16 * g + 4 * q4);
-        const f32x4 d4 =
-            *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lsv[4 * q4 + e] = l4[e];
-          dlv[4 * q4 + e] = d4[e];
-        }
-      }
-    };
     auto element = [&](auto mb_c, auto r_c) {
       constexpr int mb = decltype(mb_c)::value, r = decltype(r_c)::value;
-      float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -lsv[r]));
-      pr = (r >= mlo[mb] && r < mhi[mb]) ? pr : 0.f;
+      if constexpr (r % 4 == 0)
+        l4 = *reinterpret_cast<const f32x4*>(Lt + mb * 32 + 16 * g + r);
+      float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l4[r % 4]));
+      if constexpr (!FULL) pr = (r >= mlo[mb] && r < mhi[mb]) ? pr : 0.f;
       pvv[r] = pr;
-      dsv[r] = pr * (pa[mb][r] - dlv[r]);
+      dsv[r] = pr * pa[mb][r];
       if constexpr (r % 8 == 7) {
         constexpr int m2 = r / 8;
         f32x8 x, y;
@@ -653,7 +652,6 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       if constexpr (i >= NA && i < 2 * NA + NB) {
         constexpr int mbs = (i < 2 * NA) ? 0 : 1;
         constexpr int k = (i < 2 * NA) ? i - NA : i - 2 * NA;
-        if constexpr (k == 0) stats(ic<mbs>());
         static_for<0, EPS>([&](auto e_c) {
           element(ic<mbs>(), ic<k * EPS + decltype(e_c)::value>());
         });
@@ -662,6 +660,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
     });
+  };
+  auto compute = [&](auto slot_c, int u) {
+    const int t = t_last - u / p.G;
+    if (!wave_needs(t)) return;
+    if (tile_full(t))
+      compute_t(slot_c, std::true_type(), t);
+    else
+      compute_t(slot_c, std::false_type(), t);
   };
 
 
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
     of[ks] = __builtin_bit_cast(bf16x8, c);
   }
   const float l2 = qlive ? p.lse2[bh * p.Nqp + qi] : INFINITY;
-  const float dl = qlive ? p.delta[bh * p.Nqp + qi] : 0.f;
+  const float ndl = qlive ? p.delta[bh * p.Nqp + qi] : 0.f;
 
   f32x16 dqa[C::DB];
 #pragma unroll
@@ -912,7 +918,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
           if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
             pr = 0.f;
         }
-        dsv[r] = pr * (pa[mb][r] - dl);
+        dsv[r] = pr * (pa[mb][r] + ndl);
       }
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) {
