@@ -11,13 +11,18 @@ lse).  Per-launch durations come from HIP events recorded on the stream the
 kernels run on.  The fp64 CPU oracle is timed on a bounded sample of the
 prefill workload as a reported baseline.
 
+Besides the step it times, back to back, the backward pass of the headline
+prefill and the 1 < Nq < Nk and local-window workloads (`--no-extra` skips
+them).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
-                       [--no-cpu-baseline] [--copy-probe MIB]
+                       [--no-cpu-baseline] [--no-extra] [--copy-probe MIB]
        python bench.py --fold-traffic FETCH.csv WRITE.csv
 Prints one JSON line.
 
-HBM traffic: two rocprofv3 counter runs of a short bench with
-`--copy-probe 1024` (one with `--pmc FETCH_SIZE`, one with
+HBM traffic: two rocprofv3 counter runs of a short bench with `--no-extra
+--copy-probe 1024` (so that the only launches of the kernels are the step's;
+one run with `--pmc FETCH_SIZE`, one with
 `--pmc WRITE_SIZE`, each with `--output-format csv`) record the counters for
 the attention kernels and for a plain device-to-device copy of known size;
 `--fold-traffic` scales each kernel's counters by what the copy read and wrote
