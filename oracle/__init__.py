@@ -47,3 +47,4 @@ from .sdpa import (  # noqa: F401
 )
 from .sdpa_bwd import attention_backward  # noqa: F401
 from . import brute  # noqa: F401
+from . import fp8  # noqa: F401

@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 from tests import oracle_bwd_checks as obc
+from tests import oracle_fp8_checks as ofc
 from tests import oracle_checks as oc
 
 
@@ -111,3 +112,8 @@ def test_padding_contents_never_read():
 @pytest.mark.parametrize("check", obc.BWD_CHECKS, ids=lambda c: c.__name__)
 def test_backward_oracle_pin(check):
     check(oracle.attention_backward)
+
+
+@pytest.mark.parametrize("check", ofc.FP8_CHECKS, ids=lambda c: c.__name__)
+def test_fp8_oracle_pin(check):
+    check(oracle.fp8)
