@@ -46,6 +46,7 @@ METRIC = ("attention fwd TFLOP/s (bf16 causal prefill) + decode HBM GB/s, "
           "% of roofline")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "prefill": "transformer_self_attention_attn_amd/csrc/prefill_bf16.hip",
@@ -365,6 +366,37 @@ def main():
                "workload": "gqa-causal-prefill, dO = N(0,1) seed [3, 1]"}
         del gout, gq, gk, gv
 
+    # FP8 forward of the headline prefill: operands quantized once (block
+    # scales, Q and K rotated), then the forward kernel on the codes alone;
+    # algorithmic FLOPs as for bf16, against the dense FP8 peak
+    fp8 = None
+    if not args.no_extra:
+        sg = torch.from_numpy(synth.make_signs(wp.d, 3)).to(dev)
+
+        def quant(i):
+            return mi.fp8_quantize(P[0], P[1], P[2], seqlens=P[3], signs=sg)
+        z = quant(0)
+        fo8 = torch.empty_like(P[0])
+        fl8 = torch.empty(P[0].shape[:3], dtype=torch.float32, device=dev)
+
+        def fwd8(i):
+            mi.attn_fp8(z, causal=True, seqlens=P[3], out=fo8, lse=fl8)
+        for i in range(args.warmup):
+            fwd8(i)
+        prot8 = reps(fwd8)
+        protq = reps(quant)
+        tf8 = flops / (prot8["trimmed_mean_ms"] * 1e-3) / 1e12
+        fp8 = {"value": round(tf8, 2), "unit": "TFLOP/s",
+               "frac": round(tf8 / PEAK_FP8_TFLOPS, 4),
+               "peak": PEAK_FP8_TFLOPS,
+               "algorithmic_flop_per_launch": flops,
+               "trimmed_mean_ms": round(prot8["trimmed_mean_ms"], 5),
+               "quantize_ms": round(protq["trimmed_mean_ms"], 5),
+               "kernel": "attn_fp8_kernel<128, 8>",
+               "workload": "gqa-causal-prefill, E4M3 codes with 64-row "
+                           "block scales, Q and K rotated"}
+        del z, fo8, fl8
+
     # Nq new rows against a longer key sequence, and the local-window
     # variants: each workload on its own, `reps` launches, HIP events around
     # each; decode shapes in GB/s, the others in TFLOP/s
@@ -477,6 +509,8 @@ def main():
     }
     if bwd:
         line["backward"] = bwd
+    if fp8:
+        line["fp8"] = fp8
     if extra:
         line["nq_lt_nk"] = extra
     if masks:

@@ -145,6 +145,45 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int causal, int window_left, int window_right, int sinks,
              const int* seqlens, void* stream);
 
+/* FP8 path (the FlashAttention-3 review page's FP8 sections: E4M3 operands,
+ * block quantization, incoherent processing).
+ *
+ * attn_fp8_quantize: bf16 q, k, v (layouts and seqlens as for attn_fwd) to
+ * E4M3 codes and float32 block scales.  With `signs` (device pointer to d
+ * entries +1/-1, or NULL) Q and K are first multiplied by M = diag(signs) H,
+ * H the Sylvester Hadamard matrix with entries +-1 (so Q'' K''^T = d Q K^T;
+ * pass rotated = 1 to attn_fwd_fp8); V is never rotated.  Each 64-row block
+ * of a (batch, head) gets scale s = amax / 448 (amax over its valid rows; 0
+ * for an empty block) and codes E4M3(x * 448 / amax), rounded to nearest
+ * even, in float32.  per_tensor = 1 instead uses one amax per tensor (the
+ * baseline of the page's accuracy comparison).  Outputs (device, caller
+ * owned; Nkp = Nk rounded up to 64):
+ *   q8  [B][Hq][Nq][d] bytes           sq [B][Hq][ceil(Nq/64)] float
+ *   k8  [B][Hkv][Nkp][d] bytes         sk [B][Hkv][Nkp/64] float
+ *   v8t [B][Hkv][Nkp/64][d][64] bytes  sv [B][Hkv][Nkp/64] float
+ * (v8t holds each 64-key tile of V transposed).  Rows past the valid length
+ * and dead query rows hold code 0.  q8, k8, v8t 16-byte aligned.
+ *
+ * attn_fwd_fp8: attention of the dequantized operands, o (bf16) and lse as
+ * attn_fwd_masked computes them from q, k, v, with the same mask arguments;
+ * `scale` is the caller's softmax scale (divided by d inside when rotated).
+ * Both products run on FP8 matrix cores with fp32 accumulation; the
+ * probabilities enter the second product as E4M3 (times 256 and the tile's
+ * V scale relative to the head's largest).  Errors as attn_fwd_masked, plus
+ * MIATTN_ERR_INVALID for null or misaligned quantized buffers. */
+int attn_fp8_quantize(const void* q, const void* k, const void* v, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int d,
+                      const int* seqlens, const signed char* signs,
+                      int per_tensor, void* q8, float* sq, void* k8,
+                      float* sk, void* v8t, float* sv, void* stream);
+
+int attn_fwd_fp8(const void* q8, const float* sq, const void* k8,
+                 const float* sk, const void* v8t, const float* sv, void* o,
+                 float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int rotated, int causal, int window_left,
+                 int window_right, int sinks, const int* seqlens,
+                 void* stream);
+
 /* Message for the calling thread's most recent non-OK status ("" if none).
  * The pointer stays valid until the thread's next failing call. */
 const char* attn_last_error(void);

@@ -7,6 +7,9 @@ Recipe: numpy Generator(PCG64(seed)); draw, in this order,
      each multiplied by the workload's amplitude;
 then cast to the storage dtype (bf16: round to nearest even, done by torch).
 The fp32 copies returned for the oracle hold exactly the values the GPU sees.
+With outlier_channels > 0, that many channels (distinct, drawn next) of
+both Q and K are multiplied by outlier_mag, a few large channels shared by
+queries and keys.
 The output gradient dO of the backward pass comes from its own stream,
 Generator(PCG64([seed, 1])): float32 standard normals of the query shape,
 cast the same way.
@@ -40,6 +43,10 @@ def make_inputs(w, seed, pad_fill="draw"):
     ks = (w.B, w.Hkv, w.Nk, w.d)
     arrs = [_draw(rng, qs, w.amp), _draw(rng, ks, w.amp),
             _draw(rng, ks, w.amp)]
+    if w.outlier_channels:
+        ch = rng.choice(w.d, size=w.outlier_channels, replace=False)
+        arrs[0][..., ch] *= np.float32(w.outlier_mag)
+        arrs[1][..., ch] *= np.float32(w.outlier_mag)
     if pad_fill == "nan":
         lens = seqlens if seqlens is not None else np.full(w.B, w.Nk)
         for b in range(w.B):
@@ -76,3 +83,10 @@ def make_dout(w, seed, pad_fill="draw"):
     tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     t = torch.from_numpy(a).to(tdt).contiguous()
     return t, (a if tdt == torch.float32 else t.to(torch.float32).numpy())
+
+
+def make_signs(d, seed):
+    """The random diagonal of the FP8 path's incoherent processing: d
+    entries +1 / -1 (int8), from Generator(PCG64([seed, 2]))."""
+    rng = np.random.Generator(np.random.PCG64([seed, 2]))
+    return rng.choice(np.array([-1, 1], dtype=np.int8), size=d)

@@ -28,6 +28,8 @@ class Workload:
     len_lo: int = 0       # valid lengths drawn uniformly from [len_lo, len_hi]
     len_hi: int = 0       # (both 0: every sequence is full length)
     amp: float = 1.0      # Q, K, V = amp * N(0, 1)
+    outlier_channels: int = 0  # channels of Q and K scaled by outlier_mag
+    outlier_mag: float = 1.0
 
     @property
     def padded(self):

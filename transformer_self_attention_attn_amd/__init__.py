@@ -27,8 +27,8 @@ MIATTN_ERR_HIP = -3
 MIATTN_ERR_NOMEM = -4
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_masked",
-           "attn_fwd_masked_f32", "attn_bwd", "attn_last_error",
-           "attn_release")
+           "attn_fwd_masked_f32", "attn_bwd", "attn_fp8_quantize",
+           "attn_fwd_fp8", "attn_last_error", "attn_release")
 
 _lib = None
 
@@ -62,6 +62,12 @@ def load():
     lib.attn_fwd_masked_f32.restype = ci
     lib.attn_bwd.argtypes = [vp] * 9 + [ci] * 6 + [cf] + [ci] * 4 + [vp, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_fp8_quantize.argtypes = [vp] * 3 + [ci] * 6 + [vp, vp, ci] + \
+        [vp] * 7
+    lib.attn_fp8_quantize.restype = ci
+    lib.attn_fwd_fp8.argtypes = [vp] * 8 + [ci] * 6 + [cf] + [ci] * 5 + \
+        [vp, vp]
+    lib.attn_fwd_fp8.restype = ci
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_release.argtypes = []
@@ -108,6 +114,23 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
                            Hkv, Nq, Nk, d, scale, int(causal), window_left,
                            window_right, sinks, seqlens or None,
                            stream or None)
+
+
+def attn_fp8_quantize(q, k, v, B, Hq, Hkv, Nq, Nk, d, seqlens, signs,
+                      per_tensor, q8, sq, k8, sk, v8t, sv, stream):
+    return load().attn_fp8_quantize(q, k, v, B, Hq, Hkv, Nq, Nk, d,
+                                    seqlens or None, signs or None,
+                                    int(per_tensor), q8, sq, k8, sk, v8t,
+                                    sv, stream or None)
+
+
+def attn_fwd_fp8(q8, sq, k8, sk, v8t, sv, o, lse, B, Hq, Hkv, Nq, Nk, d,
+                 scale, rotated, causal, window_left, window_right, sinks,
+                 seqlens, stream):
+    return load().attn_fwd_fp8(q8, sq, k8, sk, v8t, sv, o, lse or None, B,
+                               Hq, Hkv, Nq, Nk, d, scale, int(rotated),
+                               int(causal), window_left, window_right, sinks,
+                               seqlens or None, stream or None)
 
 
 def attn_last_error():
@@ -216,3 +239,76 @@ def attn_backward(q, k, v, o, lse, dout, *, causal=False, window=0,
     if rc != MIATTN_OK:
         raise MiattnError(rc, attn_last_error())
     return dq, dk, dv
+
+
+def fp8_quantize(q, k, v, *, seqlens=None, signs=None, per_tensor=False,
+                 stream=None):
+    """E4M3 codes and block scales of bfloat16 GPU tensors q, k, v (see
+    attn_fp8_quantize in include/miattn.h).  signs: int8 GPU tensor of d
+    entries +-1 (rotate Q and K) or None.  Returns a dict with q8, sq, k8,
+    sk, v8t, sv, and `rotated`."""
+    import torch
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or \
+                not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-d bfloat16 GPU "
+                             "tensors")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    nkp = (Nk + 63) // 64 * 64
+    dev = q.device
+    out = dict(
+        q8=torch.empty((B, Hq, Nq, d), dtype=torch.uint8, device=dev),
+        sq=torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32,
+                       device=dev),
+        k8=torch.empty((B, Hkv, nkp, d), dtype=torch.uint8, device=dev),
+        sk=torch.empty((B, Hkv, nkp // 64), dtype=torch.float32, device=dev),
+        v8t=torch.empty((B, Hkv, nkp // 64, d, 64), dtype=torch.uint8,
+                        device=dev),
+        sv=torch.empty((B, Hkv, nkp // 64), dtype=torch.float32, device=dev),
+        rotated=signs is not None)
+    sgn = 0
+    if signs is not None:
+        if signs.dtype != torch.int8 or not signs.is_cuda or \
+                signs.numel() != d:
+            raise ValueError("signs must be an int8 GPU tensor of d entries")
+        sgn = signs.data_ptr()
+    sl = 0 if seqlens is None else seqlens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = attn_fp8_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq,
+                           Hkv, Nq, Nk, d, sl, sgn, per_tensor,
+                           out["q8"].data_ptr(), out["sq"].data_ptr(),
+                           out["k8"].data_ptr(), out["sk"].data_ptr(),
+                           out["v8t"].data_ptr(), out["sv"].data_ptr(),
+                           stream)
+    if rc != MIATTN_OK:
+        raise MiattnError(rc, attn_last_error())
+    out["shape"] = (B, Hq, Hkv, Nq, Nk, d)
+    return out
+
+
+def attn_fp8(z, *, causal=False, window=0, seqlens=None, scale=None,
+             window_right=0, sinks=0, out=None, lse=None, stream=None):
+    """Attention on the output of fp8_quantize; returns (o bf16, lse)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = z["shape"]
+    dev = z["q8"].device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    sl = 0 if seqlens is None else seqlens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = attn_fwd_fp8(z["q8"].data_ptr(), z["sq"].data_ptr(),
+                      z["k8"].data_ptr(), z["sk"].data_ptr(),
+                      z["v8t"].data_ptr(), z["sv"].data_ptr(),
+                      out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                      float(scale), z["rotated"], causal, int(window),
+                      int(window_right), int(sinks), sl, stream)
+    if rc != MIATTN_OK:
+        raise MiattnError(rc, attn_last_error())
+    return out, lse

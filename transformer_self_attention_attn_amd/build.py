@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmiattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip",
-           "bwd_bf16.hip"]
+           "bwd_bf16.hip", "fp8.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

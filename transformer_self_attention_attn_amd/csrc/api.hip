@@ -251,6 +251,62 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
   return MIATTN_OK;
 }
 
+int attn_fp8_quantize(const void* q, const void* k, const void* v, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int d,
+                      const int* seqlens, const signed char* signs,
+                      int per_tensor, void* q8, float* sq, void* k8,
+                      float* sk, void* v8t, float* sv, void* stream) {
+  const char* fn = "attn_fp8_quantize";
+  // shape checks as for the forward (q stands in for o)
+  int rc = validate(fn, q, k, v, q, nullptr, B, Hq, Hkv, Nq, Nk, d, 1.0f, 0,
+                    0, 0, 0, false);
+  if (rc != MIATTN_OK) return rc;
+  if (!q8 || !sq || !k8 || !sk || !v8t || !sv)
+    return fail(MIATTN_ERR_INVALID,
+                "%s: q8, sq, k8, sk, v8t and sv must be non-null", fn);
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) ||
+      (reinterpret_cast<uintptr_t>(sq) | reinterpret_cast<uintptr_t>(sk) |
+       reinterpret_cast<uintptr_t>(sv)) & 3u)
+    return fail(MIATTN_ERR_INVALID,
+                "%s: q8, k8, v8t must be 16-byte aligned, the scales 4-byte",
+                fn);
+  const miattn::Problem p =
+      make_problem(B, Hq, Hkv, Nq, Nk, d, 1.0f, 0, 0, 0, 0, seqlens);
+  const hipError_t e = miattn::launch_fp8_quantize(
+      q, k, v, p, signs, per_tensor, q8, sq, k8, sk, v8t, sv,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
+int attn_fwd_fp8(const void* q8, const float* sq, const void* k8,
+                 const float* sk, const void* v8t, const float* sv, void* o,
+                 float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int rotated, int causal, int window_left,
+                 int window_right, int sinks, const int* seqlens,
+                 void* stream) {
+  const char* fn = "attn_fwd_fp8";
+  int rc = validate(fn, q8, k8, v8t, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                    causal, window_left, window_right, sinks, false);
+  if (rc != MIATTN_OK) return rc;
+  if (!sq || !sk || !sv)
+    return fail(MIATTN_ERR_INVALID, "%s: sq, sk and sv must be non-null", fn);
+  if ((reinterpret_cast<uintptr_t>(sq) | reinterpret_cast<uintptr_t>(sk) |
+       reinterpret_cast<uintptr_t>(sv)) & 3u)
+    return fail(MIATTN_ERR_INVALID, "%s: the scales must be 4-byte aligned",
+                fn);
+  const miattn::Problem p =
+      make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
+                   window_right, sinks, seqlens);
+  const hipError_t e = miattn::launch_fwd_fp8(
+      q8, sq, k8, sk, v8t, sv, o, lse, p, rotated,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MIATTN_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
 const char* attn_last_error(void) { return g_err; }
 
 void attn_release(void) {

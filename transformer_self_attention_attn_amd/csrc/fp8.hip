@@ -1,0 +1,752 @@
+// FP8 attention on gfx950: block quantization with incoherent processing,
+// and a forward kernel whose two matrix products run on FP8 matrix cores.
+//
+// What is computed (the FlashAttention-3 review page's FP8 sections: block
+// quantization and incoherent processing):
+//   Q'' = Q D H, K'' = K D H      (optional; D = diag(signs), H the
+//                                  Sylvester Hadamard matrix, entries +-1:
+//                                  Q'' K''^T = d Q K^T, the softmax scale is
+//                                  divided by d)
+//   every 64-row block of Q'', K'', V of one (batch, head) is scaled by
+//   448 / amax (amax over its valid rows) and rounded to E4M3; the block's
+//   scale amax / 448 is kept
+//   O = softmax(scale * deq(Q) deq(K)^T + mask) deq(V), lse as for attn_fwd
+// E4M3 is the OCP variant the hardware converts to: round to nearest even,
+// 448 the largest finite value.
+//
+// Storage of the quantized operands (bytes; Nkp = Nk rounded up to 64):
+//   q8  [B][Hq][Nq][d]          sq [B][Hq][ceil(Nq/64)]
+//   k8  [B][Hkv][Nkp][d]        sk [B][Hkv][Nkp/64]
+//   v8t [B][Hkv][Nkp/64][d][64] sv [B][Hkv][Nkp/64]   (each 64-key tile of V
+//                                                      stored transposed)
+// Rows past the valid length (and dead query rows) hold code 0.
+//
+// Quantizer: one workgroup per 64-row block.  A row of d values is spread
+// over a wavefront, d/64 per lane; the Hadamard transform runs as butterfly
+// stages of width 1, 2, ..., d/2 (within a lane while the width is below
+// d/64, else with the lane whose index differs in one bit), in float32, in
+// that order, so every value is the same float32 the reference computes.
+// Block amax by wave then workgroup reduction; codes by v_cvt_pk_fp8_f32.
+//
+// Forward kernel: the bf16 forward kernel's decomposition (wave = 32 query
+// rows, 64-key tiles, transposed products) with FP8 operands:
+//   S^T = K Q''^T      v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales),
+//                      A = K rows from LDS, B = Q'' rows held in registers
+//   p = exp2(S^T * sq * sk_t * c - m) with the running maximum m moved once
+//   a score passes it by 2^0.5; w = p * (sv_t / sv_max) * 256 is rounded to
+//   E4M3 (the tile's V scale folded into P; 256 keeps small weights out of
+//   the subnormal range, and p <= 2^0.5 keeps w below 448)
+//   O^T += V^T W^T     A = V^T rows of the transposed tile, B = W^T straight
+//                      from the S^T accumulator layout
+//   O = O^T * sv_max / 256 / l
+// Tiles come by direct-to-LDS buffer loads into two ring slots; the 16-byte
+// chunks of every LDS row are permuted by an XOR of row bits so that the
+// operand reads are free of bank conflicts.
+#include "kernels.h"
+
+#include <cmath>
+#include <type_traits>
+
+typedef int fp8_i32x4 __attribute__((ext_vector_type(4)));
+
+// The direct-to-LDS buffer load, declared by its intrinsic name (see the
+// backward kernels for why the resource is four plain ints).
+__device__ void miattn_fp8_buffer_load_lds(
+    fp8_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+    int voffset, int soffset, int offset,
+    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+namespace miattn {
+namespace fp8_impl {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+constexpr int kBlk = 64;        // rows of a quantization block and of a tile
+constexpr int kWR = 32;         // query rows per wavefront
+constexpr int kXcds = 8;
+// Lazy-rescale threshold (log2 units): a probability may reach 2^kTau
+// before the running maximum moves, and 2^kTau * kPScale must stay within
+// E4M3's 448.
+constexpr float kTau = 0.5f;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kPScale = 256.0f;
+
+// ---------------------------------------------------------------------------
+// shared helpers
+
+struct Seq {
+  int L, Lq, off;
+};
+__device__ inline Seq seq_of(const int* seqlens, int Nq, int Nk, int b) {
+  int L = Nk;
+  if (seqlens) {
+    L = seqlens[b];
+    L = L < 0 ? 0 : (L > Nk ? Nk : L);
+  }
+  const int Lq = (Nq == Nk) ? L : Nq;
+  return {L, Lq, L - Lq};
+}
+
+// Keys of a live row at position pos: below hc; of those the window keys
+// [lo, hw) and the sink keys [0, sk).
+struct RowKeys {
+  int hc, hw, lo, sk;
+};
+__device__ inline RowKeys keys_of_row(const Seq& s, int causal, int wl,
+                                      int wr, int sinks, bool live, int pos) {
+  if (!live) return {0, 0, 0, 0};
+  RowKeys r;
+  r.hc = max(0, causal ? min(s.L, pos + 1) : s.L);
+  r.hw = wr > 0 ? max(0, min(r.hc, pos + wr)) : r.hc;
+  r.lo = wl > 0 ? max(0, pos - wl + 1) : 0;
+  r.sk = min(sinks, r.hc);
+  return r;
+}
+
+// A-operand row order of the 32x32 product (lane group g of the accumulator
+// then holds the 16 consecutive rows 16g .. 16g+15 of each 32-row block).
+__device__ inline int mfma_row(int m) {
+  return (m >> 5) * 32 + ((m >> 2) & 1) * 16 + ((m & 31) >> 3) * 4 + (m & 3);
+}
+
+// Chunk permutations (16-byte chunks): K tile rows are 128 bytes (d = 128)
+// or 64 bytes (d = 64) and are read 16 rows at a time in mfma_row order;
+// V^T tile rows are 64 bytes read 16 consecutive rows at a time.
+template <int D>
+__device__ inline int swz_k(int r) {
+  if constexpr (D == 128)
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+  else
+    return ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+}
+__device__ inline int swz_v(int r) { return (r >> 2) & 3; }
+
+__device__ inline fp8_i32x4 rsrc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  fp8_i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+__device__ inline void barrier_nofence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ inline float wave_maxf(float x) {
+  for (int s = 32; s > 0; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// quantizer
+
+struct QuantParams {
+  const uint16_t* x;   // bf16 [B][H][N][d]
+  uint8_t* codes;      // layout below
+  float* scales;       // [B][H][nblk]
+  const int* seqlens;
+  const signed char* signs;  // d entries (+-1) or null: no rotation
+  int B, H, N, d, Nq, Nk;    // Nq, Nk: the attention problem's sizes
+  int is_q;            // rows valid: live query rows (else the valid length)
+  int transposed;      // codes as [B][H][nblk][d][64] (V), else [B][H][Npad][d]
+  int Npad;            // rows per head in `codes` (N, or Nk rounded to 64)
+  int nblk;            // blocks per head
+  int mode;            // 0: block scale; 1: amax only; 2: preset amax
+};
+
+// mode 0: codes and scale from the block's own amax; mode 1: writes the
+// block's amax to scales[] and nothing else; mode 2: reads amax from
+// scales[] (all blocks of the tensor set to one value), writes codes and the
+// scale amax / 448.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantParams p) {
+  constexpr int E = D / 64;  // values per lane of a row
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlk];
+  const int blk = blockIdx.x % p.nblk;
+  const int bh = blockIdx.x / p.nblk;
+  const int b = bh / p.H;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
+  const int valid = p.is_q ? s.Lq : s.L;
+  const int r0 = blk * kBlk;
+
+  float sg[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    sg[e] = p.signs ? (float)p.signs[lane * E + e] : 1.0f;
+
+  // rows r0 + wave*16 .. +15 of the block: load, rotate, track |max|
+  float v[16][E];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + wave * 16 + i;
+    const bool ok = r < valid && r < p.N;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[i][e] = 0.f;
+    if (ok) {
+      const uint16_t* src = p.x + ((size_t)bh * p.N + r) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        v[i][e] = __uint_as_float((unsigned)src[e] << 16);
+    }
+    if (p.signs) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[i][e] *= sg[e];
+      // butterflies of width h: element j pairs with j ^ h; the lower one
+      // becomes a + b, the upper one a - b
+#pragma unroll
+      for (int h = 1; h < D; h <<= 1) {
+        if (h < E) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if ((e & h) == 0) {
+              const float a = v[i][e], c = v[i][e + h];
+              v[i][e] = a + c;
+              v[i][e + h] = a - c;
+            }
+        } else {
+          const int lb = h / E;  // partner lane differs in this bit
+          const bool upper = (lane & lb) != 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float o = __shfl_xor(v[i][e], lb);
+            v[i][e] = upper ? o - v[i][e] : v[i][e] + o;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+  }
+  amax = wave_maxf(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float* sp = p.scales + (size_t)bh * p.nblk + blk;
+  if (p.mode == 1) {
+    if (threadIdx.x == 0) *sp = amax;
+    return;
+  }
+  if (p.mode == 2) {
+    amax = *sp;  // every thread reads the preset amax before it is replaced
+    __syncthreads();
+  }
+  const float mul = amax > 0.f ? kE4M3Max / amax : 0.f;
+  if (threadIdx.x == 0) *sp = amax / kE4M3Max;
+
+  // codes: row-major rows, or through LDS into the transposed tile
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rl = wave * 16 + i;
+    const int r = r0 + rl;
+    unsigned w = 0;
+    if constexpr (E == 2) {
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] * mul, v[i][1] * mul, 0u,
+                                          false);
+    } else {
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] * mul, 0.f, 0u, false);
+    }
+    if (p.transposed) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        tile[(lane * E + e) * kBlk + rl] = (uint8_t)(w >> (8 * e));
+    } else if (r < p.Npad) {
+      uint8_t* dst = p.codes + ((size_t)bh * p.Npad + r) * D + lane * E;
+      if constexpr (E == 2)
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w & 0xffffu);
+      else
+        *dst = (uint8_t)(w & 0xffu);
+    }
+  }
+  if (p.transposed) {
+    __syncthreads();
+    uint8_t* dst = p.codes + ((size_t)bh * p.nblk + blk) * D * kBlk;
+    for (int o = threadIdx.x * 16; o < D * kBlk; o += 256 * 16)
+      *reinterpret_cast<u32x4*>(dst + o) =
+          *reinterpret_cast<const u32x4*>(tile + o);
+  }
+}
+
+// Per-tensor amax: reduces the block amaxes of one tensor and writes the
+// maximum back into every block's slot (then mode 2 quantizes with it).
+__global__ __launch_bounds__(256) void fp8_tensor_amax_kernel(float* scales,
+                                                              int n) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, scales[i]);
+  m = wave_maxf(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256) scales[i] = m;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+
+struct Fp8Params {
+  const uint8_t* q8;
+  const float* sq;
+  const uint8_t* k8;
+  const float* sk;
+  const uint8_t* v8t;
+  const float* sv;
+  uint16_t* o;
+  float* lse;
+  const int* seqlens;
+  int B, Hq, Hkv, Nq, Nk, Nkp, G, nqb, total;
+  int causal, window, window_right, sinks;
+  float c;  // scale * log2(e) (divided by d for rotated operands)
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
+  constexpr int QB = kWR * NW;
+  constexpr int KT = kBlk * D;  // bytes of a K tile and of a V^T tile
+  constexpr int KS = D / 64;    // k-steps of the S product
+  constexpr int DB = D / 32;    // 32-row blocks of O^T
+  constexpr int LOADS = 2 * KT / 1024;  // wave loads per step (K and V^T)
+  constexpr int LW = (LOADS + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs0[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs1[KT];
+  __shared__ float red_sv[NW];
+  auto kslot = [&](auto s) -> uint8_t* {
+    if constexpr (decltype(s)::value == 0) return Ks0; else return Ks1;
+  };
+  auto vslot = [&](auto s) -> uint8_t* {
+    if constexpr (decltype(s)::value == 0) return Vs0; else return Vs1;
+  };
+
+  // block -> (batch, K/V head, query block, head of the group), blocks of a
+  // group on one XCD; causal blocks heaviest first
+  const int n = p.total;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int lid = xcd * (n / kXcds) + min(xcd, n % kXcds) + bid / kXcds;
+  const int per_grp = p.G * p.nqb;
+  const int grp = lid / per_grp;
+  const int r0g = lid - grp * per_grp;
+  const int qrank = r0g / p.G;
+  const int hh = r0g - qrank * p.G;
+  const int qb = p.causal ? (p.nqb - 1 - qrank) : qrank;
+  const int b = grp / p.Hkv;
+  const int hk = grp - b * p.Hkv;
+  const int h = hk * p.G + hh;
+  const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ql = lane & 31;
+  const int g = lane >> 5;
+  const int q0 = qb * QB;
+  const int qw0 = q0 + wave * kWR;
+  const int qi = qw0 + ql;
+  const bool qlive = qi < s.Lq;
+  const RowKeys rk = keys_of_row(s, p.causal, p.window, p.window_right,
+                                 p.sinks, qlive, qi + s.off);
+
+  // tiles of the workgroup: sink tiles, then window tiles (one run when
+  // they meet); step u visits tile_of(u)
+  const int rows_end = min(q0 + QB, s.Lq);
+  int nA = 0, tB0 = 0, nt = 0;
+  if (rows_end > q0) {
+    const RowKeys f = keys_of_row(s, p.causal, p.window, p.window_right,
+                                  p.sinks, true, q0 + s.off);
+    const RowKeys l = keys_of_row(s, p.causal, p.window, p.window_right,
+                                  p.sinks, true, rows_end - 1 + s.off);
+    int tw0 = f.lo / kBlk, tw1 = (l.hw + kBlk - 1) / kBlk;
+    if (l.hw <= f.lo) tw0 = tw1 = 0;
+    const int ts1 = (l.sk + kBlk - 1) / kBlk;
+    if (ts1 >= tw0) {
+      nA = max(ts1, tw1);
+      nt = nA;
+    } else {
+      nA = ts1;
+      tB0 = tw0;
+      nt = ts1 + (tw1 - tw0);
+    }
+  }
+  auto tile_of = [&](int u) { return u < nA ? u : tB0 + (u - nA); };
+  const int wend = min(qw0 + kWR, s.Lq);
+  const bool wlive = wend > qw0;
+  RowKeys wf = {0, 0, 0, 0}, wl = {0, 0, 0, 0};
+  if (wlive) {
+    wf = keys_of_row(s, p.causal, p.window, p.window_right, p.sinks, true,
+                     qw0 + s.off);
+    wl = keys_of_row(s, p.causal, p.window, p.window_right, p.sinks, true,
+                     wend - 1 + s.off);
+  }
+  auto wave_needs = [&](int t) {
+    const int j0 = t * kBlk;
+    return wlive && ((j0 < wl.hw && j0 + kBlk > wf.lo) || j0 < wl.sk);
+  };
+  auto tile_full = [&](int t) {
+    const int j0 = t * kBlk;
+    return (j0 >= wl.lo && j0 + kBlk <= wf.hw) || j0 + kBlk <= wf.sk;
+  };
+
+  // the largest V tile scale of this (batch, K/V head): every tile's V
+  // scale enters P relative to it
+  const int ntk = p.Nkp / kBlk;
+  const float* svh = p.sv + (size_t)(b * p.Hkv + hk) * ntk;
+  const float* skh = p.sk + (size_t)(b * p.Hkv + hk) * ntk;
+  float svm = 0.f;
+  for (int t = tid; t < ntk; t += 64 * NW) svm = fmaxf(svm, svh[t]);
+  svm = wave_maxf(svm);
+  if (lane == 0) red_sv[wave] = svm;
+  __syncthreads();
+  svm = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) svm = fmaxf(svm, red_sv[w]);
+  const float inv_svm = svm > 0.f ? kPScale / svm : 0.f;
+
+  // Q'' of this lane's row as B operand: 32 bytes per k-step
+  const size_t bhq = (size_t)b * p.Hq + h;
+  i32x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 lo4 = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
+    if (qlive) {
+      const uint8_t* src = p.q8 + (bhq * p.Nq + qi) * D + 64 * ks + 32 * g;
+      lo4 = *reinterpret_cast<const u32x4*>(src);
+      hi4 = *reinterpret_cast<const u32x4*>(src + 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[ks][e] = (int)lo4[e];
+      qf[ks][4 + e] = (int)hi4[e];
+    }
+  }
+  const float sqr = qlive ? p.sq[bhq * ((p.Nq + kBlk - 1) / kBlk) + qi / kBlk]
+                          : 0.f;
+  const float crow = sqr * p.c;
+
+  // LDS operand offsets: K rows (two 16-byte chunks per k-step), V^T rows
+  // (chunks g and 2 + g: keys 16g .. 16g+15 and 32+16g .. 32+16g+15)
+  int koff[2][KS][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = mfma_row(mb * 32 + ql);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        koff[mb][ks][hf] =
+            row * D + 16 * ((4 * ks + 2 * g + hf) ^ swz_k<D>(row));
+  }
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int row = db * 32 + ql;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      voff[db][hf] = row * 64 + 16 * ((2 * hf + g) ^ swz_v(row));
+  }
+
+  // direct-to-LDS loads: wave load u2 = wave + NW*m; the first KT/1024 fill
+  // the K tile, the rest the V^T tile; each lane's source offset in a tile
+  // is fixed
+  unsigned toffs[LW];
+#pragma unroll
+  for (int m = 0; m < LW; ++m) {
+    const int u2 = wave + NW * m;
+    const int i = u2 < KT / 1024 ? u2 : u2 - KT / 1024;
+    const int sl = i * 64 + lane;
+    if (u2 < KT / 1024) {
+      const int row = sl / (D / 16);
+      const int c = (sl % (D / 16)) ^ swz_k<D>(row);
+      toffs[m] = (unsigned)(row * D + 16 * c);
+    } else {
+      const int row = sl / 4;
+      const int c = (sl % 4) ^ swz_v(row);
+      toffs[m] = (unsigned)(row * 64 + 16 * c);
+    }
+  }
+  const size_t kvh = (size_t)(b * p.Hkv + hk) * p.Nkp * D;
+  const fp8_i32x4 krs = rsrc(p.k8 + kvh, p.Nkp * D);
+  const fp8_i32x4 vrs = rsrc(p.v8t + kvh, p.Nkp * D);
+  auto issue = [&](auto slot_c, int u) {
+    const unsigned tb = (unsigned)(tile_of(u) * KT);
+#pragma unroll
+    for (int m = 0; m < LW; ++m) {
+      const int u2 = wave + NW * m;
+      if (u2 < KT / 1024)
+        miattn_fp8_buffer_load_lds(
+            krs, (lds_void*)(kslot(slot_c) + u2 * 1024), 16, toffs[m] + tb,
+            0, 0, 0);
+      else if (u2 < LOADS)
+        miattn_fp8_buffer_load_lds(
+            vrs, (lds_void*)(vslot(slot_c) + (u2 - KT / 1024) * 1024), 16,
+            toffs[m] + tb, 0, 0, 0);
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float M = -INFINITY;  // running maximum (log2 units)
+  float l = 0.f;        // this lane's half of the running sum
+  const f32x16 zero = {};
+
+  auto compute = [&](auto slot_c, int u) {
+    const int t = tile_of(u);
+    if (!wave_needs(t)) return;
+    const uint8_t* Kt = kslot(slot_c);
+    const uint8_t* Vt = vslot(slot_c);
+    // S^T = K Q''^T
+    f32x16 sa[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(Kt + koff[mb][ks][0]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(Kt + koff[mb][ks][1]);
+        i32x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (int)a0[e];
+          a[4 + e] = (int)a1[e];
+        }
+        sa[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a, qf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    // scores in log2 units, masked, and the tile maximum
+    const float cs = crow * skh[t];
+    const int j0 = t * kBlk;
+    const bool full = tile_full(t);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sa[mb][r] * cs;
+        if (!full) {
+          const int jj = j0 + mb * 32 + 16 * g + r;
+          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
+            x = -INFINITY;
+        }
+        sa[mb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
+      const float mn = fmaxf(M, mx);
+      const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      M = mn;
+    }
+    const float mu = (M == -INFINITY) ? 0.f : M;
+    // P, the row sums, and W = P * sv_t / sv_max * 256 as E4M3 (B operand:
+    // bytes 0..15 keys 16g + r, bytes 16..31 keys 32 + 16g + r)
+    const float vr = svh[t] * inv_svm;
+    i32x8 wb;
+    float ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        float pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pr[e] = __builtin_amdgcn_exp2f(sa[mb][r + e] - mu);
+          ls += pr[e];
+        }
+        unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * vr, pr[1] * vr,
+                                                     0u, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * vr, pr[3] * vr, w, true);
+        wb[mb * 4 + r / 4] = (int)w;
+      }
+    l += ls;
+    // O^T += V^T W^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(Vt + voff[db][0]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(Vt + voff[db][1]);
+      i32x8 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (int)a0[e];
+        a[4 + e] = (int)a1[e];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a, wb, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
+  };
+
+  if (nt > 0) {
+    issue(ic<0>(), 0);
+    wait_vm0();
+    barrier_nofence();
+    auto step = [&](auto slot_c, int u) {
+      constexpr int S = decltype(slot_c)::value;
+      if (u + 1 < nt) issue(ic<1 - S>(), u + 1);
+      compute(slot_c, u);
+      wait_vm0();
+      barrier_nofence();
+    };
+    for (int u = 0; u < nt; u += 2) {
+      step(ic<0>(), u);
+      if (u + 1 < nt) step(ic<1>(), u + 1);
+    }
+  }
+
+  // O = O^T * sv_max / 256 / l, lse = (M + log2 l) ln 2
+  const float lt = l + __shfl_xor(l, 32);
+  if (qi < p.Nq) {
+    const bool any = qlive && lt > 0.f;
+    const float f = any ? svm / (kPScale * lt) : 0.f;
+    uint16_t* orow = p.o + (bhq * p.Nq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int quad = 0; quad < 4; ++quad) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = oacc[db][4 * quad + e] * f;
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + quad * 8 + 4 * g) =
+            __builtin_convertvector(v4, bf16x4);
+      }
+    if (g == 0 && p.lse)
+      p.lse[bhq * p.Nq + qi] =
+          any ? (M + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t quant_one(QuantParams q, hipStream_t st, bool per_tensor) {
+  const unsigned grid = (unsigned)(q.B * q.H * q.nblk);
+  if (!per_tensor) {
+    q.mode = 0;
+    hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
+    return hipGetLastError();
+  }
+  q.mode = 1;
+  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
+  hipLaunchKernelGGL(fp8_tensor_amax_kernel, dim3(1), dim3(256), 0, st,
+                     q.scales, (int)grid);
+  q.mode = 2;
+  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
+  return hipGetLastError();
+}
+
+}  // namespace fp8_impl
+
+using namespace fp8_impl;
+
+hipError_t launch_fp8_quantize(const void* q, const void* k, const void* v,
+                               const Problem& pr, const signed char* signs,
+                               int per_tensor, void* q8, float* sq, void* k8,
+                               float* sk, void* v8t, float* sv,
+                               hipStream_t stream) {
+  const int nkp = (pr.Nk + kBlk - 1) / kBlk * kBlk;
+  QuantParams base = {};
+  base.seqlens = pr.seqlens;
+  base.B = pr.B;
+  base.Nq = pr.Nq;
+  base.Nk = pr.Nk;
+  base.d = pr.d;
+  QuantParams a = base;  // Q
+  a.x = static_cast<const uint16_t*>(q);
+  a.codes = static_cast<uint8_t*>(q8);
+  a.scales = sq;
+  a.signs = signs;
+  a.H = pr.Hq;
+  a.N = pr.Nq;
+  a.is_q = 1;
+  a.transposed = 0;
+  a.Npad = pr.Nq;
+  a.nblk = (pr.Nq + kBlk - 1) / kBlk;
+  QuantParams bk = base;  // K
+  bk.x = static_cast<const uint16_t*>(k);
+  bk.codes = static_cast<uint8_t*>(k8);
+  bk.scales = sk;
+  bk.signs = signs;
+  bk.H = pr.Hkv;
+  bk.N = pr.Nk;
+  bk.is_q = 0;
+  bk.transposed = 0;
+  bk.Npad = nkp;
+  bk.nblk = nkp / kBlk;
+  QuantParams c = bk;  // V: never rotated, tiles transposed
+  c.x = static_cast<const uint16_t*>(v);
+  c.codes = static_cast<uint8_t*>(v8t);
+  c.scales = sv;
+  c.signs = nullptr;
+  c.transposed = 1;
+  hipError_t e;
+  const bool pt = per_tensor != 0;
+  if (pr.d == 128) {
+    if ((e = quant_one<128>(a, stream, pt)) != hipSuccess) return e;
+    if ((e = quant_one<128>(bk, stream, pt)) != hipSuccess) return e;
+    return quant_one<128>(c, stream, pt);
+  }
+  if ((e = quant_one<64>(a, stream, pt)) != hipSuccess) return e;
+  if ((e = quant_one<64>(bk, stream, pt)) != hipSuccess) return e;
+  return quant_one<64>(c, stream, pt);
+}
+
+hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
+                          const float* sk, const void* v8t, const float* sv,
+                          void* o, float* lse, const Problem& pr, int rotated,
+                          hipStream_t stream) {
+  Fp8Params p;
+  p.q8 = static_cast<const uint8_t*>(q8);
+  p.sq = sq;
+  p.k8 = static_cast<const uint8_t*>(k8);
+  p.sk = sk;
+  p.v8t = static_cast<const uint8_t*>(v8t);
+  p.sv = sv;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.seqlens = pr.seqlens;
+  p.B = pr.B;
+  p.Hq = pr.Hq;
+  p.Hkv = pr.Hkv;
+  p.Nq = pr.Nq;
+  p.Nk = pr.Nk;
+  p.Nkp = (pr.Nk + kBlk - 1) / kBlk * kBlk;
+  p.G = pr.Hq / pr.Hkv;
+  p.causal = pr.causal;
+  p.window = pr.window;
+  p.window_right = pr.window_right;
+  p.sinks = pr.sinks;
+  p.c = pr.scale * 1.4426950408889634f / (rotated ? (float)pr.d : 1.0f);
+  constexpr int NW = 8;
+  p.nqb = (pr.Nq + kWR * NW - 1) / (kWR * NW);
+  p.total = pr.B * pr.Hq * p.nqb;
+  if (pr.d == 128)
+    hipLaunchKernelGGL((attn_fp8_kernel<128, NW>), dim3(p.total),
+                       dim3(64 * NW), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fp8_kernel<64, NW>), dim3(p.total),
+                       dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace miattn

@@ -40,6 +40,18 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v,
                            void* dq, void* dk, void* dv, const Problem& p,
                            void* ws, hipStream_t stream);
 
+// FP8 path: quantization (bf16 q, k, v -> E4M3 codes and block scales, Q and
+// K rotated when `signs` is non-null) and the forward kernel on the codes.
+hipError_t launch_fp8_quantize(const void* q, const void* k, const void* v,
+                               const Problem& p, const signed char* signs,
+                               int per_tensor, void* q8, float* sq, void* k8,
+                               float* sk, void* v8t, float* sv,
+                               hipStream_t stream);
+hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
+                          const float* sk, const void* v8t, const float* sv,
+                          void* o, float* lse, const Problem& p, int rotated,
+                          hipStream_t stream);
+
 // fp32 path (any Nq in {1, Nk}).
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v,
                            float* o, float* lse, const Problem& p,
