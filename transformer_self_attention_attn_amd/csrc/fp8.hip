@@ -312,7 +312,8 @@ struct Fp8Params {
   const int* seqlens;
   int B, Hq, Hkv, Nq, Nk, Nkp, G, nqb, total;
   int causal, window, window_right, sinks;
-  float c;  // scale * log2(e) (divided by d for rotated operands)
+  float c;  // |scale| * log2(e) (divided by d for rotated operands)
+  unsigned qsign;  // 0x80808080 when the scale is negative: Q codes negated
 };
 
 template <int D, int NW>
@@ -427,8 +428,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     u32x4 lo4 = {0u, 0u, 0u, 0u}, hi4 = {0u, 0u, 0u, 0u};
     if (qlive) {
       const uint8_t* src = p.q8 + (bhq * p.Nq + qi) * D + 64 * ks + 32 * g;
-      lo4 = *reinterpret_cast<const u32x4*>(src);
-      hi4 = *reinterpret_cast<const u32x4*>(src + 16);
+      lo4 = *reinterpret_cast<const u32x4*>(src) ^ p.qsign;
+      hi4 = *reinterpret_cast<const u32x4*>(src + 16) ^ p.qsign;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -438,7 +439,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
   }
   const float sqr = qlive ? p.sq[bhq * ((p.Nq + kBlk - 1) / kBlk) + qi / kBlk]
                           : 0.f;
-  const float crow = sqr * p.c;
+  // row factor of the scores (log2 units); a zero block scale means zero
+  // scores, and a tiny positive factor keeps masked scores at -inf
+  const float crow = fmaxf(sqr * p.c, 1e-30f);
 
   // LDS operand offsets: K rows (two 16-byte chunks per k-step), V^T rows
   // (chunks g and 2 + g: keys 16g .. 16g+15 and 32+16g .. 32+16g+15)
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
   const size_t kvh = (size_t)(b * p.Hkv + hk) * p.Nkp * D;
   const fp8_i32x4 krs = rsrc(p.k8 + kvh, p.Nkp * D);
   const fp8_i32x4 vrs = rsrc(p.v8t + kvh, p.Nkp * D);
-  auto issue = [&](auto slot_c, int u) {
+  auto issue_k = [&](auto slot_c, int u) {
     const unsigned tb = (unsigned)(tile_of(u) * KT);
 #pragma unroll
     for (int m = 0; m < LW; ++m) {
@@ -493,7 +496,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
         miattn_fp8_buffer_load_lds(
             krs, (lds_void*)(kslot(slot_c) + u2 * 1024), 16, toffs[m] + tb,
             0, 0, 0);
-      else if (u2 < LOADS)
+    }
+  };
+  auto issue_v = [&](auto slot_c, int u) {
+    const unsigned tb = (unsigned)(tile_of(u) * KT);
+#pragma unroll
+    for (int m = 0; m < LW; ++m) {
+      const int u2 = wave + NW * m;
+      if (u2 >= KT / 1024 && u2 < LOADS)
         miattn_fp8_buffer_load_lds(
             vrs, (lds_void*)(vslot(slot_c) + (u2 - KT / 1024) * 1024), 16,
             toffs[m] + tb, 0, 0, 0);
@@ -509,15 +519,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
   float l = 0.f;        // this lane's half of the running sum
   const f32x16 zero = {};
 
-  auto compute = [&](auto slot_c, int u) {
-    const int t = tile_of(u);
-    if (!wave_needs(t)) return;
+  // S^T of tile t (raw accumulators; the score is acc * crow * sk_t)
+  auto qk = [&](auto slot_c, f32x16(&s2)[2]) {
     const uint8_t* Kt = kslot(slot_c);
-    const uint8_t* Vt = vslot(slot_c);
-    // S^T = K Q''^T
-    f32x16 sa[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(Kt + koff[mb][ks][0]);
@@ -528,32 +534,37 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
           a[e] = (int)a0[e];
           a[4 + e] = (int)a1[e];
         }
-        sa[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a, qf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0, 127, 0, 127);
+        s2[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a, qf[ks], ks == 0 ? zero : s2[mb], 0, 0, 0, 127, 0, 127);
       }
-    }
-    // scores in log2 units, masked, and the tile maximum
+  };
+
+  // softmax of tile t on its raw scores sc: W = P * vr as E4M3 in wb
+  // (bytes 0..15: keys 16g + r, 16..31: keys 32 + 16g + r), row sums in l
+  auto softmax = [&](int t, f32x16(&sc)[2], i32x8& wb) {
     const float cs = crow * skh[t];
-    const int j0 = t * kBlk;
-    const bool full = tile_full(t);
-    float mx = -INFINITY;
+    if (!tile_full(t)) {
+      const int j0 = t * kBlk;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = j0 + mb * 32 + 16 * g + r;
+          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
+            sc[mb][r] = -INFINITY;
+        }
+    }
+    float mr = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sa[mb][r] * cs;
-        if (!full) {
-          const int jj = j0 + mb * 32 + 16 * g + r;
-          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
-            x = -INFINITY;
-        }
-        sa[mb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sc[mb][r]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32));
+    const float mx = mr * cs;  // cs > 0: the largest score of the row
     if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
       const float mn = fmaxf(M, mx);
-      const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+      const float alpha =
+          (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -561,29 +572,31 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       M = mn;
     }
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    // P, the row sums, and W = P * sv_t / sv_max * 256 as E4M3 (B operand:
-    // bytes 0..15 keys 16g + r, bytes 16..31 keys 32 + 16g + r)
-    const float vr = svh[t] * inv_svm;
-    i32x8 wb;
+    // w = 2^(acc cs - M) * vr = 2^(acc cs + (log2 vr - M)); the V ratio is
+    // kept above 2^-100 so that a tile of zero V still counts in l
+    const float vr = fmaxf(svh[t] * inv_svm, 0x1p-100f);
+    const float lv = __builtin_amdgcn_logf(vr) - ((M == -INFINITY) ? 0.f : M);
     float ls = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        float pr[4];
+        float w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pr[e] = __builtin_amdgcn_exp2f(sa[mb][r + e] - mu);
-          ls += pr[e];
+          w[e] = __builtin_amdgcn_exp2f(fmaf(sc[mb][r + e], cs, lv));
+          ls += w[e];
         }
-        unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * vr, pr[1] * vr,
-                                                     0u, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * vr, pr[3] * vr, w, true);
-        wb[mb * 4 + r / 4] = (int)w;
+        unsigned u = __builtin_amdgcn_cvt_pk_fp8_f32(w[0], w[1], 0u, false);
+        u = __builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], u, true);
+        wb[mb * 4 + r / 4] = (int)u;
       }
-    l += ls;
-    // O^T += V^T W^T
+    l += ls * (1.0f / vr);
+  };
+
+  // O^T += V^T W^T over tile t's keys
+  auto pv = [&](auto slot_c, const i32x8& wb) {
+    const uint8_t* Vt = vslot(slot_c);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x4 a0 = *reinterpret_cast<const u32x4*>(Vt + voff[db][0]);
@@ -599,20 +612,37 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     }
   };
 
+  // Step t: loads of K(t+2) and V(t+1) go out; the S^T product of tile t+1
+  // runs on the matrix cores while the softmax of tile t (whose S^T the
+  // previous step formed) runs on the vector units; then O^T += V^T W^T of
+  // tile t.  K(t) and V(t) live in slot t % 2.
+  // Prologue: K(0), V(0), K(1) resident, S^T(0) formed.
+  f32x16 sa[2], sb[2];
   if (nt > 0) {
-    issue(ic<0>(), 0);
+    issue_k(ic<0>(), 0);
+    issue_v(ic<0>(), 0);
+    if (1 < nt) issue_k(ic<1>(), 1);
     wait_vm0();
     barrier_nofence();
-    auto step = [&](auto slot_c, int u) {
-      constexpr int S = decltype(slot_c)::value;
-      if (u + 1 < nt) issue(ic<1 - S>(), u + 1);
-      compute(slot_c, u);
+    if (wave_needs(tile_of(0))) qk(ic<0>(), sa);
+    auto step = [&](auto par_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+      constexpr int P = decltype(par_c)::value;
+      if (t + 2 < nt) issue_k(ic<P>(), t + 2);
+      if (t + 1 < nt) issue_v(ic<1 - P>(), t + 1);
+      const int tt = tile_of(t);
+      const bool need = wave_needs(tt);
+      if (t + 1 < nt && wave_needs(tile_of(t + 1))) qk(ic<1 - P>(), sn);
+      if (need) {
+        i32x8 wb;
+        softmax(tt, sc, wb);
+        pv(ic<P>(), wb);
+      }
       wait_vm0();
       barrier_nofence();
     };
-    for (int u = 0; u < nt; u += 2) {
-      step(ic<0>(), u);
-      if (u + 1 < nt) step(ic<1>(), u + 1);
+    for (int t = 0; t < nt; t += 2) {
+      step(ic<0>(), t, sa, sb);
+      if (t + 1 < nt) step(ic<1>(), t + 1, sb, sa);
     }
   }
 
@@ -736,7 +766,9 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
   p.window = pr.window;
   p.window_right = pr.window_right;
   p.sinks = pr.sinks;
-  p.c = pr.scale * 1.4426950408889634f / (rotated ? (float)pr.d : 1.0f);
+  p.c = fabsf(pr.scale) * 1.4426950408889634f /
+        (rotated ? (float)pr.d : 1.0f);
+  p.qsign = pr.scale < 0.f ? 0x80808080u : 0u;
   constexpr int NW = 8;
   p.nqb = (pr.Nq + kWR * NW - 1) / (kWR * NW);
   p.total = pr.B * pr.Hq * p.nqb;
