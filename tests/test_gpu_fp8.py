@@ -157,3 +157,72 @@ def test_fp8_rmse_block_rotated_vs_per_tensor():
     gu.say(f"  rmse block+rotation={res['block+rotation']:.4e} "
            f"per-tensor={res['per-tensor']:.4e} ratio={ratio:.2f}")
     assert ratio > 1.5, res
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.07], ids=["scale0", "negscale"])
+def test_fp8_scale_edge(scale):
+    """scale 0: every allowed key weighs the same; a negative scale takes
+    the Q codes' sign flip inside the kernel."""
+    w = W("fp8-scale-edge-d128", 2, 4, 2, 200, 200, 128, "bf16", True,
+          len_lo=30, len_hi=200)
+    gu.say(f"[gpu] fp8 forward {w.name} scale={scale}")
+    x = synth.make_inputs(w, 54)
+    signs = synth.make_signs(w.d, 54)
+    z, sl = gpu_quant(w, x, signs, False)
+    o, lse = mi.attn_fp8(z, seqlens=sl, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    ref = ref_quant(w, x, signs, False)
+    ro, rl = oracle.fp8.attention_quantized(
+        ref["q"], ref["k"], ref["v"], scale=scale, rotated=True, causal=True,
+        seqlens=x["seqlens"])
+    compare_o(f"{w.name} scale={scale}", o, lse, ro, rl)
+
+
+def test_fp8_nan_padding_is_never_read():
+    """NaN in every padded row of Q, K and V changes no code, no scale and
+    no output."""
+    w = W("fp8-nan-pad-d64", 3, 4, 2, 300, 300, 64, "bf16", True, len_lo=1,
+          len_hi=300)
+    gu.say(f"[gpu] fp8 {w.name}")
+    signs = synth.make_signs(w.d, 55)
+    xs = synth.make_inputs(w, 55)
+    xn = synth.make_inputs(w, 55, pad_fill="nan")
+    za, sl = gpu_quant(w, xs, signs, False)
+    zb, _ = gpu_quant(w, xn, signs, False)
+    for key in ("q8", "sq", "k8", "sk", "v8t", "sv"):
+        assert torch.equal(za[key], zb[key]), key
+    oa, la = mi.attn_fp8(za, seqlens=sl, scale=w.scale, causal=True)
+    ob, lb = mi.attn_fp8(zb, seqlens=sl, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    assert torch.all(torch.isfinite(ob))
+
+
+def test_fp8_full_size_gqa_causal_prefill():
+    """gqa-causal-prefill at full size: every code and scale against the
+    reference, and sampled output rows against the exact attention of the
+    dequantized operands."""
+    w = synth.by_name("gqa-causal-prefill")
+    gu.say(f"[gpu] fp8 {w.name} (full size)")
+    x = synth.make_inputs(w, 3)
+    signs = synth.make_signs(w.d, 3)
+    z, sl = gpu_quant(w, x, signs, False)
+    ref = ref_quant(w, x, signs, False)
+    assert np.array_equal(z["q8"].cpu().numpy(), ref["q"][0])
+    assert np.array_equal(z["sq"].cpu().numpy(), ref["q"][1])
+    assert np.array_equal(z["k8"].cpu().numpy(), ref["k"][0])
+    assert np.array_equal(z["sk"].cpu().numpy(), ref["k"][1])
+    assert np.array_equal(natural_v(z["v8t"], w.Nk).cpu().numpy(),
+                          ref["v"][0])
+    assert np.array_equal(z["sv"].cpu().numpy(), ref["v"][1])
+    o, lse = mi.attn_fp8(z, seqlens=sl, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1003)
+    picks = gu.sample_rows(w, None, rng)
+    qd = oracle.fp8.dequantize(*ref["q"])
+    kd = oracle.fp8.dequantize(*ref["k"])
+    vd = oracle.fp8.dequantize(*ref["v"])
+    ro, rl = oracle.attention_rows(qd, kd, vd, picks, scale=w.scale / w.d,
+                                   causal=True)
+    idx = tuple(np.array(picks).T)
+    compare_o(f"{w.name} sampled", o[idx], lse[idx], ro, rl)
