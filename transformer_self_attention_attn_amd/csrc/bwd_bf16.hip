@@ -51,19 +51,13 @@
 #include <cmath>
 #include <type_traits>
 
-typedef int bwd_i32x4 __attribute__((ext_vector_type(4)));
+#include "device_common.h"
 
-// The direct-to-LDS buffer load (buffer_load_dword* ... lds), declared by
-// its intrinsic name with the resource as four plain ints: written with the
-// resource-type builtins, these kernels lost their host-side launch stubs
-// in this compiler.
-__device__ void miattn_buffer_load_lds(
-    bwd_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
-    int voffset, int soffset, int offset,
-    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 namespace miattn {
 namespace bwd_impl {
+
+using namespace dev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -75,13 +69,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int N>
-using ic = std::integral_constant<int, N>;
-
 constexpr int kRT = 64;    // rows of a streamed tile (queries or keys)
 constexpr int kWR = 32;    // rows a wave owns (keys in dK/dV, queries in dQ)
-constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies
-constexpr int kBig = 1 << 30;
 
 struct BwdParams {
   const uint16_t* q;
@@ -126,119 +115,6 @@ __device__ inline int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
 }
 
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(ic<I>());
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Valid length and row positions of batch b: rows i < Lq are live and row i
-// sits at position i + off (Nq == Nk: the first L rows; otherwise the last Nq
-// positions of the sequence).
-struct Seq {
-  int L, Lq, off;
-};
-__device__ inline Seq seq_of(const BwdParams& p, int b) {
-  int L = p.Nk;
-  if (p.seqlens) {
-    L = p.seqlens[b];
-    L = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
-  }
-  const int Lq = (p.Nq == p.Nk) ? L : p.Nq;
-  return {L, Lq, L - Lq};
-}
-
-// Query rows [lo, hi) that may see key j (empty when lo >= hi).  Row i at
-// position pos sees key j < L when pos >= j under the causal mask and, unless
-// j is a sink key, j - window_right < pos < j + window (each limit off when
-// 0).
-__device__ inline void rows_of_key(const BwdParams& p, const Seq& s, int j,
-                                   int& lo, int& hi) {
-  if (j >= s.L) {
-    lo = s.Lq;
-    hi = 0;
-    return;
-  }
-  int plo = p.causal ? j : -kBig;
-  int phi = kBig;
-  if (j >= p.sinks) {
-    if (p.window_right > 0) plo = max(plo, j - p.window_right + 1);
-    if (p.window > 0) phi = j + p.window;
-  }
-  lo = max(0, plo - s.off);
-  hi = min(s.Lq, phi - s.off);
-}
-
-// Keys of the row at position pos (live rows): those below hc, and of them
-// the window keys [lo, hw) and the sink keys [0, sk).
-struct RowKeys {
-  int hc, hw, lo, sk;
-};
-__device__ inline RowKeys keys_of_row(const BwdParams& p, const Seq& s,
-                                      bool live, int pos) {
-  RowKeys r;
-  if (!live) return {0, 0, 0, 0};
-  r.hc = max(0, p.causal ? min(s.L, pos + 1) : s.L);
-  r.hw = p.window_right > 0 ? max(0, min(r.hc, pos + p.window_right)) : r.hc;
-  r.lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
-  r.sk = min(p.sinks, r.hc);
-  return r;
-}
-
-// Row of a 32-row MFMA A-operand block that holds tile row m: with this order
-// the 32x32 accumulator gives lane group g (lanes 32g .. 32g+31) the 16
-// consecutive tile rows g*16 .. g*16+15 of each 32-row block.
-__device__ inline int mfma_row(int m) {
-  return (m >> 5) * 32 + ((m >> 2) & 1) * 16 + ((m & 31) >> 3) * 4 + (m & 3);
-}
-
-__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
-
-// Waits until at most n (0 .. 15, wave-uniform) vector-memory loads of this
-// wave are outstanding; other counters untouched (vmcnt is bits 3:0 here).
-__device__ inline void wait_vmcnt_rt(int n) {
-  switch (n) {
-#define MIATTN_BW(N) \
-  case N:            \
-    __builtin_amdgcn_s_waitcnt(0xF70 | (N)); \
-    break;
-    MIATTN_BW(1) MIATTN_BW(2) MIATTN_BW(3) MIATTN_BW(4) MIATTN_BW(5)
-    MIATTN_BW(6) MIATTN_BW(7) MIATTN_BW(8) MIATTN_BW(9) MIATTN_BW(10)
-    MIATTN_BW(11) MIATTN_BW(12) MIATTN_BW(13) MIATTN_BW(14) MIATTN_BW(15)
-#undef MIATTN_BW
-    default:
-      __builtin_amdgcn_s_waitcnt(0xF70);
-  }
-}
-__device__ inline void barrier_nofence() {
-  asm volatile("s_barrier" ::: "memory");
-}
-
-__device__ inline float wave_max(float x) {
-  for (int s = 32; s > 0; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
-  return x;
-}
-__device__ inline int wave_imin(int x) {
-  for (int s = 32; s > 0; s >>= 1) x = min(x, __shfl_xor(x, s));
-  return x;
-}
-__device__ inline int wave_imax(int x) {
-  for (int s = 32; s > 0; s >>= 1) x = max(x, __shfl_xor(x, s));
-  return x;
-}
-
-// Block index -> logical block: consecutive logical blocks share an XCD (and
-// its L2), so blocks of one (batch, K/V head) group meet in one cache.
-__device__ inline int xcd_block(int bid, int n) {
-  const int xcd = bid % kXcds;
-  const int slot = bid / kXcds;
-  const int per = n / kXcds;
-  const int rem = n % kXcds;
-  return xcd * per + min(xcd, rem) + slot;
-}
-
 // One wave-wide direct-to-LDS load of a [64][D] tile: wave load i fills
 // tile bytes [i*1024, +1024); lane l writes 16-byte slot s = i*64 + l, which
 // is physical chunk s % CH of row s / CH and so holds that row's logical
@@ -254,19 +130,6 @@ __device__ inline unsigned tile_src_off(int i, int lane) {
   const int r = s / C::CH;
   const int c = (s % C::CH) ^ swz<D>(r);
   return (unsigned)((r * D + c * 8) * 2);
-}
-
-// Buffer resource over `bytes` bytes at `base` (stride 0, 32-bit data
-// format): a load at or past the end reads zeros, which is how rows past the
-// valid length enter LDS as zeros.
-__device__ inline bwd_i32x4 rows_rsrc(const void* base, int bytes) {
-  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-  bwd_i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  return r;
 }
 
 // Element offset of this lane's row-wise A-operand piece: tile row
@@ -321,7 +184,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const bool valid = row < total;
   const int bh = valid ? (int)(row / p.Nqp) : 0;
   const int i = valid ? (int)(row - (long long)bh * p.Nqp) : 0;
-  const Seq s = seq_of(p, bh / p.Hq);
+  const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, bh / p.Hq);
   float lse = -INFINITY;
   if (valid && i < s.Lq) lse = p.lse[(size_t)bh * p.Nq + i];
   const bool live = valid && i < s.Lq && lse > -INFINITY;
@@ -395,7 +258,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   const int kb = lid - grp * p.nblk;
   const int b = grp / p.Hkv;
   const int hk = grp - b * p.Hkv;
-  const Seq s = seq_of(p, b);
+  const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
+  auto key_rows = [&](int key, int& lo, int& hi) {
+    rows_of_key(s, p.causal, p.window, p.window_right, p.sinks, key, lo, hi);
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,7 +276,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   // outside it is skipped) and their intersection (a tile inside it needs no
   // mask)
   int rlo, rhi;
-  rows_of_key(p, s, j, rlo, rhi);
+  key_rows(j, rlo, rhi);
   const bool kne = rlo < rhi;
   const int w_lo_min = wave_imin(kne ? rlo : kBig);
   const int w_hi_max = wave_imax(kne ? rhi : -kBig);
@@ -422,8 +288,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   if (k0 < s.L) {
     const int k1 = min(k0 + KB, s.L);
     int a_lo, a_hi, b_lo, b_hi;
-    rows_of_key(p, s, k0, a_lo, a_hi);
-    rows_of_key(p, s, k1 - 1, b_lo, b_hi);
+    key_rows(k0, a_lo, a_hi);
+    key_rows(k1 - 1, b_lo, b_hi);
     const int hi = k0 < p.sinks ? s.Lq : max(a_hi, b_hi);
     if (hi > a_lo) {
       t0 = a_lo / kRT;
@@ -480,7 +346,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
+    for (int db = 0; db < C::DB; ++db)
+      toff[half][db] = tr_off<D>(lane, half, db);
 
   // loads of step u (query head hk*G + u / nt, tile t0 + u % nt) into slot S
   // this wave's loads of a step: wave load u2 = wave + NW*m; u2 < LOADS is
@@ -757,7 +624,11 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
   const int b = grp / p.Hkv;
   const int hk = grp - b * p.Hkv;
   const int h = hk * p.G + hh;
-  const Seq s = seq_of(p, b);
+  const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
+  auto row_keys = [&](bool live, int pos) {
+    return keys_of_row(s, p.causal, p.window, p.window_right, p.sinks, live,
+                       pos);
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -768,15 +639,15 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
   const int qw0 = q0 + wave * kWR;
   const int qi = qw0 + ql;
   const bool qlive = qi < s.Lq;
-  const RowKeys rk = keys_of_row(p, s, qlive, qi + s.off);
+  const RowKeys rk = row_keys(qlive, qi + s.off);
 
   // the workgroup's tiles: sink tiles [0, ts1), then window tiles
   // [tw0, tw1), merged into one run when they meet; step u visits tile_of(u)
   const int rows_end = min(q0 + QB, s.Lq);
   int nA = 0, tB0 = 0, nt = 0;
   if (rows_end > q0) {
-    const RowKeys first = keys_of_row(p, s, true, q0 + s.off);
-    const RowKeys last = keys_of_row(p, s, true, rows_end - 1 + s.off);
+    const RowKeys first = row_keys(true, q0 + s.off);
+    const RowKeys last = row_keys(true, rows_end - 1 + s.off);
     int tw0 = first.lo / kRT, tw1 = (last.hw + kRT - 1) / kRT;
     if (last.hw <= first.lo) tw0 = tw1 = 0;
     const int ts1 = (last.sk + kRT - 1) / kRT;
@@ -796,8 +667,8 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
   const bool wlive = wend > qw0;
   RowKeys wf = {0, 0, 0, 0}, wl = {0, 0, 0, 0};
   if (wlive) {
-    wf = keys_of_row(p, s, true, qw0 + s.off);
-    wl = keys_of_row(p, s, true, wend - 1 + s.off);
+    wf = row_keys(true, qw0 + s.off);
+    wl = row_keys(true, wend - 1 + s.off);
   }
   auto wave_needs = [&](int t) {
     const int j0 = t * kRT;
@@ -841,7 +712,8 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) toff[half][db] = tr_off<D>(lane, half, db);
+    for (int db = 0; db < C::DB; ++db)
+      toff[half][db] = tr_off<D>(lane, half, db);
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
   // this wave's tile loads: wave load u2 = wave + NW*m, K tile loads first

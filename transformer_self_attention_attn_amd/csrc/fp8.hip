@@ -47,17 +47,12 @@
 #include <cmath>
 #include <type_traits>
 
-typedef int fp8_i32x4 __attribute__((ext_vector_type(4)));
-
-// The direct-to-LDS buffer load, declared by its intrinsic name (see the
-// backward kernels for why the resource is four plain ints).
-__device__ void miattn_fp8_buffer_load_lds(
-    fp8_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
-    int voffset, int soffset, int offset,
-    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+#include "device_common.h"
 
 namespace miattn {
 namespace fp8_impl {
+
+using namespace dev;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -66,56 +61,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int N>
-using ic = std::integral_constant<int, N>;
-
 constexpr int kBlk = 64;        // rows of a quantization block and of a tile
 constexpr int kWR = 32;         // query rows per wavefront
-constexpr int kXcds = 8;
 // Lazy-rescale threshold (log2 units): a probability may reach 2^kTau
 // before the running maximum moves, and 2^kTau * kPScale must stay within
 // E4M3's 448.
 constexpr float kTau = 0.5f;
 constexpr float kE4M3Max = 448.0f;
 constexpr float kPScale = 256.0f;
-
-// ---------------------------------------------------------------------------
-// shared helpers
-
-struct Seq {
-  int L, Lq, off;
-};
-__device__ inline Seq seq_of(const int* seqlens, int Nq, int Nk, int b) {
-  int L = Nk;
-  if (seqlens) {
-    L = seqlens[b];
-    L = L < 0 ? 0 : (L > Nk ? Nk : L);
-  }
-  const int Lq = (Nq == Nk) ? L : Nq;
-  return {L, Lq, L - Lq};
-}
-
-// Keys of a live row at position pos: below hc; of those the window keys
-// [lo, hw) and the sink keys [0, sk).
-struct RowKeys {
-  int hc, hw, lo, sk;
-};
-__device__ inline RowKeys keys_of_row(const Seq& s, int causal, int wl,
-                                      int wr, int sinks, bool live, int pos) {
-  if (!live) return {0, 0, 0, 0};
-  RowKeys r;
-  r.hc = max(0, causal ? min(s.L, pos + 1) : s.L);
-  r.hw = wr > 0 ? max(0, min(r.hc, pos + wr)) : r.hc;
-  r.lo = wl > 0 ? max(0, pos - wl + 1) : 0;
-  r.sk = min(sinks, r.hc);
-  return r;
-}
-
-// A-operand row order of the 32x32 product (lane group g of the accumulator
-// then holds the 16 consecutive rows 16g .. 16g+15 of each 32-row block).
-__device__ inline int mfma_row(int m) {
-  return (m >> 5) * 32 + ((m >> 2) & 1) * 16 + ((m & 31) >> 3) * 4 + (m & 3);
-}
 
 // Chunk permutations (16-byte chunks): K tile rows are 128 bytes (d = 128)
 // or 64 bytes (d = 64) and are read 16 rows at a time in mfma_row order;
@@ -128,26 +81,6 @@ __device__ inline int swz_k(int r) {
     return ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
 }
 __device__ inline int swz_v(int r) { return (r >> 2) & 3; }
-
-__device__ inline fp8_i32x4 rsrc(const void* base, int bytes) {
-  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-  fp8_i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
-__device__ inline void barrier_nofence() {
-  asm volatile("s_barrier" ::: "memory");
-}
-
-__device__ inline float wave_maxf(float x) {
-  for (int s = 32; s > 0; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
-  return x;
-}
 
 // ---------------------------------------------------------------------------
 // quantizer
@@ -338,10 +271,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
 
   // block -> (batch, K/V head, query block, head of the group), blocks of a
   // group on one XCD; causal blocks heaviest first
-  const int n = p.total;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int lid = xcd * (n / kXcds) + min(xcd, n % kXcds) + bid / kXcds;
+  const int lid = xcd_block(blockIdx.x, p.total);
   const int per_grp = p.G * p.nqb;
   const int grp = lid / per_grp;
   const int r0g = lid - grp * per_grp;
@@ -485,15 +415,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     }
   }
   const size_t kvh = (size_t)(b * p.Hkv + hk) * p.Nkp * D;
-  const fp8_i32x4 krs = rsrc(p.k8 + kvh, p.Nkp * D);
-  const fp8_i32x4 vrs = rsrc(p.v8t + kvh, p.Nkp * D);
+  const miattn_i32x4 krs = rows_rsrc(p.k8 + kvh, p.Nkp * D);
+  const miattn_i32x4 vrs = rows_rsrc(p.v8t + kvh, p.Nkp * D);
   auto issue_k = [&](auto slot_c, int u) {
     const unsigned tb = (unsigned)(tile_of(u) * KT);
 #pragma unroll
     for (int m = 0; m < LW; ++m) {
       const int u2 = wave + NW * m;
       if (u2 < KT / 1024)
-        miattn_fp8_buffer_load_lds(
+        miattn_buffer_load_lds(
             krs, (lds_void*)(kslot(slot_c) + u2 * 1024), 16, toffs[m] + tb,
             0, 0, 0);
     }
@@ -504,7 +434,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     for (int m = 0; m < LW; ++m) {
       const int u2 = wave + NW * m;
       if (u2 >= KT / 1024 && u2 < LOADS)
-        miattn_fp8_buffer_load_lds(
+        miattn_buffer_load_lds(
             vrs, (lds_void*)(vslot(slot_c) + (u2 - KT / 1024) * 1024), 16,
             toffs[m] + tb, 0, 0, 0);
     }
