@@ -57,6 +57,13 @@ DECODE_CASES = [
     W("decode-nocausal", 2, 8, 2, 1, 600, 128, "bf16", False, len_lo=1,
       len_hi=600),
     W("decode-one-key", 2, 4, 1, 1, 1, 64, "bf16", True),
+    # more query heads per K/V head than one wavefront's 16 MFMA columns:
+    # 32 -> two chunks of 16, 24 -> two of 12, 17 (prime) -> 17 of one
+    W("decode-mqa32-d64", 2, 32, 1, 1, 900, 64, "bf16", True, len_lo=1,
+      len_hi=900),
+    W("decode-g24-d128", 2, 48, 2, 1, 700, 128, "bf16", True, len_lo=300,
+      len_hi=700),
+    W("decode-g17-d128", 1, 17, 1, 1, 600, 128, "bf16", True),
 ]
 
 

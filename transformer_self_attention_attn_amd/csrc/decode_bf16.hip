@@ -4,56 +4,62 @@
 // appended to the cache (SpAtten review page, Background - Attention-Based NLP
 // Models); the page notes this stage is memory-bound.  The query is the last
 // token of its sequence: it may see keys j < L_b (and, with a window w, only
-// j >= L_b - w).
+// j >= L_b - w; sink keys j < sinks always).
 //
-// Pass 1 (decode_split_kernel): grid = splits x (K/V head, head chunk) x batch.
-//   A workgroup owns a chunk of kChunk keys of one (batch, K/V head) and the
-//   GB query heads of that group that share it, so each K and V byte is read
-//   from HBM exactly once for all of them.  The chunk is one pass over its
-//   key rows: every group of D/8 lanes takes every (kThreads*8/D)-th row,
-//   loads its K and V together (16 B per lane each, non-temporal: the cache
-//   is streamed once) and keeps, per head, an online softmax of its own rows:
-//     s = scale * q . k       (bf16 pair dot products in fp32, summed across
-//                              the group's lanes with DPP), in log2 units;
-//     m = running maximum, moved (and l, o rescaled) only when a score
-//         exceeds it by more than 2^8;
-//     l += 2^(s - m);  o += 2^(s - m) v.
-//   A register ring keeps the next kRing-1 batches of rows in flight, and
-//   nothing waits on other lanes until the chunk ends.  Then the groups are
-//   merged (shifts to a common maximum) across lanes and, through LDS,
-//   across the wavefronts.  The workgroup writes the chunk's partial result
+// Pass 1 (decode_split_kernel): grid = (batch, K/V head, head chunk) x split,
+//   one wavefront per workgroup.  A wavefront owns a chunk of kChunk keys of
+//   one (batch, K/V head) and the (up to 16) query heads of that group that
+//   share it, so each K and V byte is read from HBM once for all of them.
+//   The heads sharing a K/V head make the step a small matrix product, so it
+//   runs on the matrix cores (16 x 16 tiles, heads padded to 16):
+//     S^T[key][head] = K_tile . Q^T        v_mfma_f32_16x16x32_bf16
+//     O^T[d][head]  += V_tile^T . P^T      v_mfma_f32_16x16x16_bf16
+//   K and V stream through a ring of kStages LDS stages (16 keys each, K and
+//   V) filled by direct-to-LDS loads issued kStages - 1 tiles ahead; the K
+//   operand is read with ds_read_b128 and the V^T operand with the
+//   transposing ds_read_b64_tr_b16, both conflict-free under a 16-byte chunk
+//   permutation of the tile rows.  Each lane holds 4 keys of one head per
+//   tile; the online softmax (base 2, the running maximum moved only when a
+//   score exceeds it by more than 2^8) needs one exchange across the 4 lane
+//   groups per tile.  The wavefront writes the chunk's partial result
 //   o_s = o / l (fp32) and lse_s = (m + log2 l) ln 2 to the workspace.
 //   Chunks that hold no allowed key exit at once.
 // Pass 2 (decode_combine_kernel): one wavefront per (batch, query head).
-//   lse = log sum_s exp(lse_s) (max-shifted) and o = sum_s exp(lse_s - lse) o_s,
-//   the softmax definition applied to a partition of the keys; written as bf16
-//   o and fp32 lse.
+//   lse = log sum_s exp(lse_s) (max-shifted) and
+//   o = sum_s exp(lse_s - lse) o_s, the softmax definition applied to a
+//   partition of the keys; written as bf16 o and fp32 lse.
 #include "kernels.h"
 
 #include <cmath>
+#include <type_traits>
+
+#include "device_common.h"
 
 namespace miattn {
 namespace {
 
+using namespace dev;
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef MIATTN_DECODE_EAGER
-#define MIATTN_DECODE_EAGER 0
-#endif
-#ifndef MIATTN_DECODE_RING
-#define MIATTN_DECODE_RING 4
-#endif
-
-constexpr int kThreads = 256;
 #ifndef MIATTN_DECODE_CHUNK
 #define MIATTN_DECODE_CHUNK 512
 #endif
-constexpr int kChunk = MIATTN_DECODE_CHUNK;  // keys per split
-constexpr int kRing = MIATTN_DECODE_RING;  // key-row batches per lane in flight + 1
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
-constexpr int kMaxGB = 8;    // query heads per workgroup
+#ifndef MIATTN_DECODE_STAGES
+#define MIATTN_DECODE_STAGES 4
+#endif
+constexpr int kChunk = MIATTN_DECODE_CHUNK;    // keys per split
+constexpr int kStages = MIATTN_DECODE_STAGES;  // LDS ring stages per wave
+constexpr int kKT = 16;          // keys per tile
+constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr int kMaxGB = 16;       // query heads per wavefront (MFMA columns)
 constexpr int kCombineWaves = 4;  // (batch, head) rows per combine workgroup
+constexpr int kNonTemporal = 2;  // cache policy of the K/V loads: streamed
 
 struct DecodeParams {
   const uint16_t* q;
@@ -91,57 +97,147 @@ __device__ inline int split_first_key(int c0, int c1, int lo, int sk) {
   return a < c1 ? a : c1;
 }
 
-template <int W>
-__device__ inline float group_sum(float x) {
-  // sum over aligned groups of W lanes (W = 8 or 16) with DPP row permutes
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                     __builtin_bit_cast(int, x), 0xB1, 0xF,
-                                     0xF, true));  // quad_perm [1,0,3,2]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                     __builtin_bit_cast(int, x), 0x4E, 0xF,
-                                     0xF, true));  // quad_perm [2,3,0,1]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                     __builtin_bit_cast(int, x), 0x141, 0xF,
-                                     0xF, true));  // row_half_mirror
-  if (W == 16)
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                       __builtin_bit_cast(int, x), 0x140, 0xF,
-                                       0xF, true));  // row_mirror
-  return x;
-}
-
 __device__ inline float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
   return x;
 }
-__device__ inline float wave_sum(float x) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+
+// 16-byte chunk c of tile row r (rows of D * 2 bytes) sits at chunk
+// c ^ tile_swz(r): with it the K operand reads (16 rows, one chunk, per 16
+// lanes) and the V transposing reads (8 rows x 32 bytes per 32 lanes) touch
+// every LDS bank once.
+template <int D>
+__device__ inline int tile_swz(int r) {
+  if constexpr (D == 128)
+    return 2 * (r & 7) + ((r >> 3) & 1);
+  else
+    return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
 
-// K and V rows are read once per call: streaming (non-temporal) loads keep
-// them from displacing reusable lines in the caches.
-__device__ inline u32x4 load_stream(const uint16_t* ptr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+// a and b start as two copies of x; afterwards {a, b} = {x, x of lane l ^ 16}
+// (permlane16) or {x, x of lane l ^ 32} (permlane32) in every lane.  Inline
+// assembly with two distinct registers: given the same value twice, the
+// builtins were folded to a single result.
+__device__ inline void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+// max / sum over the four lanes n, n + 16, n + 32, n + 48
+__device__ inline float quad_max(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float quad_sum(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = a + b;
+  a = x;
+  b = x;
+  swap32(a, b);
+  return a + b;
 }
 
-__device__ inline float bf16_lo(unsigned w) {
-  return __builtin_bit_cast(float, w << 16);
+// One tile's matrix operands from LDS: the K rows (ds_read_b128) and the V^T
+// blocks (ds_read_b64_tr_b16) of D = 128 or 64, issued together and awaited
+// in the same block.  Written as assembly so that the compiler's own wait
+// insertion, which cannot tell the stage being read from the stages being
+// filled by direct-to-LDS loads at a loop head, adds no wait for those loads:
+// the explicit wait on the load counter before each tile orders them.
+__device__ inline void lds_operands(bf16x8 (&ka)[4], i16x4 (&va)[8],
+                                    const unsigned (&kad)[4],
+                                    const unsigned (&vad)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(ka[2]), "=&v"(ka[3]),
+        "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]),
+        "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]), "=&v"(va[7])
+      : "v"(kad[0]), "v"(kad[1]), "v"(kad[2]), "v"(kad[3]), "v"(vad[0]),
+        "v"(vad[1]), "v"(vad[2]), "v"(vad[3]), "v"(vad[4]), "v"(vad[5]),
+        "v"(vad[6]), "v"(vad[7])
+      : "memory");
 }
-__device__ inline float bf16_hi(unsigned w) {
-  return __builtin_bit_cast(float, w & 0xffff0000u);
+__device__ inline void lds_operands(bf16x8 (&ka)[2], i16x4 (&va)[4],
+                                    const unsigned (&kad)[2],
+                                    const unsigned (&vad)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b64_tr_b16 %2, %8\n\t"
+      "ds_read_b64_tr_b16 %3, %9\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(va[0]), "=&v"(va[1]),
+        "=&v"(va[2]), "=&v"(va[3])
+      : "v"(kad[0]), "v"(kad[1]), "v"(vad[0]), "v"(vad[1]), "v"(vad[2]),
+        "v"(vad[3])
+      : "memory");
 }
 
-template <int D, int GB>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
-    DecodeParams p) {
-  constexpr int LPK = D / 8;           // lanes per key row (16 B each)
-  constexpr int GPW = 64 / LPK;        // row groups per wavefront
-  constexpr int NWV = kThreads / 64;   // wavefronts per workgroup
-  constexpr int RPB = kThreads / LPK;  // key rows per batch (one per group)
-  constexpr int R = kRing;             // batches held in registers
-  __shared__ float red_o[NWV][GB * D];
-  __shared__ float red_ml[NWV][2 * GB];
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int TB = kKT * D * 2;    // bytes of one K (or V) tile
+  constexpr int TL = TB / 1024;      // wave-wide 16-byte loads per tile
+  constexpr int NJ = D / 32;         // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 16;        // 16-row blocks of O^T
+  constexpr int S = kStages;
+  constexpr int ROW = D * 2;         // bytes per tile row
+  static_assert(TL * 1024 == TB, "tile loads");
+  static_assert(S >= 2 && S <= 6, "stages");
+  // one LDS object per stage and operand: the compiler keeps per-object
+  // alias scopes, so reads of one stage need not wait for the loads that
+  // fill another
+#define MIATTN_DSTAGE(X, I) \
+  __shared__ __attribute__((aligned(16))) unsigned char X##I[S > I ? TB : 16];
+  MIATTN_DSTAGE(Ks, 0) MIATTN_DSTAGE(Ks, 1) MIATTN_DSTAGE(Ks, 2)
+  MIATTN_DSTAGE(Ks, 3) MIATTN_DSTAGE(Ks, 4) MIATTN_DSTAGE(Ks, 5)
+  MIATTN_DSTAGE(Vs, 0) MIATTN_DSTAGE(Vs, 1) MIATTN_DSTAGE(Vs, 2)
+  MIATTN_DSTAGE(Vs, 3) MIATTN_DSTAGE(Vs, 4) MIATTN_DSTAGE(Vs, 5)
+#undef MIATTN_DSTAGE
+  auto kst = [&](auto st_c) -> unsigned char* {
+    constexpr int ST = decltype(st_c)::value;
+    if constexpr (ST == 0) return Ks0;
+    else if constexpr (ST == 1) return Ks1;
+    else if constexpr (ST == 2) return Ks2;
+    else if constexpr (ST == 3) return Ks3;
+    else if constexpr (ST == 4) return Ks4;
+    else return Ks5;
+  };
+  auto vst = [&](auto st_c) -> unsigned char* {
+    constexpr int ST = decltype(st_c)::value;
+    if constexpr (ST == 0) return Vs0;
+    else if constexpr (ST == 1) return Vs1;
+    else if constexpr (ST == 2) return Vs2;
+    else if constexpr (ST == 3) return Vs3;
+    else if constexpr (ST == 4) return Vs4;
+    else return Vs5;
+  };
 
   // grid x = (batch, K/V head, head chunk), fastest; grid y = split.
   // Workgroups are dealt to the XCDs round-robin in launch order, so each
@@ -151,25 +247,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int b = blockIdx.x / nx;
   const int hk = (blockIdx.x - b * nx) / p.nhc;
   const int hc = blockIdx.x - b * nx - hk * p.nhc;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int dch = tid % LPK;  // 8-column chunk of the row this lane reads
-  const int grp = tid / LPK;  // row group: rows c0 + i * RPB + grp
-  const int h0 = hk * p.G + hc * GB;
-  const int nh = min(GB, p.G - hc * GB);
+  const int lane = threadIdx.x;
+  const int n = lane & 15;   // MFMA column: head (S^T, O^T), key row (K)
+  const int qg = lane >> 4;  // lane group
+  const int h0 = hk * p.G + hc * p.GB;
+  const int nh = min(p.GB, p.G - hc * p.GB);
 
-  // query fragments (8 columns of each head as bf16 pairs); issued before
-  // the valid length is known, the address does not depend on it
-  unsigned qw[GB][4];
+  // Q^T operand: head n, columns 32j + 8qg .. +7 (zero for padding heads);
+  // issued before the valid length is known, the address does not depend on it
+  bf16x8 qf[NJ];
 #pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
+  for (int j = 0; j < NJ; ++j) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (gi < nh)
+    if (n < nh)
       raw = *reinterpret_cast<const u32x4*>(
-          p.q + (size_t)(b * p.Hq + h0 + gi) * D + dch * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qw[gi][e] = raw[e];
+          p.q + (size_t)(b * p.Hq + h0 + n) * D + 32 * j + 8 * qg);
+    qf[j] = __builtin_bit_cast(bf16x8, raw);
   }
 
   int lo, L, sk;
@@ -178,151 +271,142 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int c1 = min(c0 + kChunk, L);
   const int a0 = split_first_key(c0, c1, lo, sk);
   if (a0 >= c1) return;  // no allowed key here; the combine skips this split
-  const int first = (a0 - c0) / RPB;
-  const int nb = (c1 - c0 + RPB - 1) / RPB;  // batches first .. nb-1
+  const int kt0 = c0 + (a0 - c0) / kKT * kKT;  // first key of the first tile
+  const int nt = (c1 - kt0 + kKT - 1) / kKT;   // tiles of this split
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
-  const uint16_t* kg = p.k + kv_base + dch * 8;
-  const uint16_t* vg = p.v + kv_base + dch * 8;
+  const uint16_t* kg = p.k + kv_base;
+  const uint16_t* vg = p.v + kv_base;
 
-  // ring of R batches: batch i sits in slot (i - first) % R.  Every lane
-  // loads on every step (no branch around the loads, so the hardware's
-  // in-order load counter tells exactly when a slot has arrived); a row
-  // outside [a0, c1) is clamped to an allowed row, read again from cache,
+  // direct-to-LDS placement: load i of a tile fills bytes [i*1024, +1024);
+  // lane l writes 16-byte slot i*64 + l = (row r, chunk pc), which holds
+  // logical chunk pc ^ tile_swz(r) of key row r.  Every lane loads on every
+  // step (the in-order load counter then tells when a stage has landed); a
+  // row outside [a0, c1) is clamped to an allowed row, read again from cache,
   // and masked out of the softmax.
-  u32x4 kr[R], vr[R];
-  auto issue = [&](int i, u32x4& kd, u32x4& vd) {
-    const int key = min(max(c0 + i * RPB + grp, a0), c1 - 1);
-    kd = load_stream(kg + (size_t)key * D);
-    vd = load_stream(vg + (size_t)key * D);
+  int lrow[TL];
+  int lcol[TL];
+#pragma unroll
+  for (int i = 0; i < TL; ++i) {
+    const int slot = i * 64 + lane;
+    lrow[i] = slot / CH;
+    lcol[i] = ((slot % CH) ^ tile_swz<D>(slot / CH)) * 8;
+  }
+  auto issue = [&](int t, auto st_c) {
+    const int key0 = kt0 + t * kKT;
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+      const int key = min(max(key0 + lrow[i], a0), c1 - 1);
+      const size_t off = (size_t)key * D + lcol[i];
+      __builtin_amdgcn_global_load_lds(
+          kg + off, (lds_void*)(kst(st_c) + i * 1024), 16, 0, kNonTemporal);
+      __builtin_amdgcn_global_load_lds(
+          vg + off, (lds_void*)(vst(st_c) + i * 1024), 16, 0, kNonTemporal);
+    }
   };
-#pragma unroll
-  for (int r = 0; r < R - 1; ++r) issue(first + r, kr[r], vr[r]);
 
-  // per row group and head: running max m (log2 units), sum l, output o
-  float m[GB], l[GB], o[GB][8];
+  // operand read offsets within a stage: K row n, logical chunk 4j + qg
+  // (ds_read_b128); V^T block db: lane n of group qg addresses row
+  // 4qg + n/4, columns 16db + 4(n%4) .. +3 (ds_read_b64_tr_b16 hands lane n
+  // column 16db + n of rows 4qg .. 4qg + 3)
+  int koff[NJ], voff[NDB];
 #pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
-    m[gi] = -INFINITY;
-    l[gi] = 0.f;
+  for (int j = 0; j < NJ; ++j)
+    koff[j] = n * ROW + ((4 * j + qg) ^ tile_swz<D>(n)) * 16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[gi][e] = 0.f;
+  for (int db = 0; db < NDB; ++db) {
+    const int r = 4 * qg + (n >> 2);
+    const int col = 16 * db + 4 * (n & 3);
+    voff[db] = r * ROW + ((col >> 3) ^ tile_swz<D>(r)) * 16 + (n & 1) * 8;
   }
 
-  // whole rounds of R steps; steps past the last batch are fully masked
-  for (int i0 = first; i0 < nb; i0 += R) {
+  f32x4 oacc[NDB];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = i0 + r;
-      {
-        // keep R - 1 batches in flight: refill the slot freed last step
-        issue(i + R - 1, kr[(r + R - 1) % R], vr[(r + R - 1) % R]);
-        const int key = c0 + i * RPB + grp;
-        const bool ok = key >= a0 && key < c1 && (key >= lo || key < sk);
-        float sc[GB];
+  for (int db = 0; db < NDB; ++db) oacc[db] = {0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY;  // running maximum of head n (log2 units)
+  float lsum = 0.f;     // this lane's share of head n's sum
+
+  static_for<0, S - 1>([&](auto r_c) { issue(r_c, r_c); });
+  for (int i0 = 0; i0 < nt; i0 += S) {
+    static_for<0, S>([&](auto r_c) {
+      constexpr int r = decltype(r_c)::value;
+      const int t = i0 + r;
+      // keep S - 1 tiles in flight: refill the stage read last step
+      issue(t + S - 1, ic<(r + S - 1) % S>());
+      wait_vm<2 * TL * (S - 1)>();  // tile t has landed
+      if (t < nt) {
+        // LDS byte addresses of this stage's operands
+        const unsigned kb = (unsigned)(uintptr_t)(lds_void*)kst(r_c);
+        const unsigned vb = (unsigned)(uintptr_t)(lds_void*)vst(r_c);
+        unsigned kad[NJ], vad[NDB];
 #pragma unroll
-        for (int gi = 0; gi < GB; ++gi) {
-          float acc = 0.f;
+        for (int j = 0; j < NJ; ++j) kad[j] = kb + koff[j];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned kw = kr[r][e];
-            const unsigned qv = qw[gi][e];
-            acc = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2, kw), __builtin_bit_cast(bf16x2, qv),
-                acc, false);
-          }
-          acc = group_sum<LPK>(acc);
-          sc[gi] = ok ? acc * p.c : -INFINITY;
-        }
-        // move the running maximum only when a score exceeds it by more
-        // than 2^tau (any common shift of a row's scores is exact)
-#if MIATTN_DECODE_EAGER
-        {
-#else
-        bool grow = false;
+        for (int db = 0; db < NDB; ++db) vad[db] = vb + voff[db];
+        bf16x8 ka[NJ];
+        i16x4 va[NDB];
+        lds_operands(ka, va, kad, vad);
+        // S^T = K . Q^T: lane (qg, n) gets keys 4qg + e of head n
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int gi = 0; gi < GB; ++gi) grow |= sc[gi] > m[gi] + kTau;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#endif
-#pragma unroll
-          for (int gi = 0; gi < GB; ++gi) {
-            const float mn = fmaxf(m[gi], sc[gi]);
-            const float a =
-                mn == m[gi] ? 1.0f : __builtin_amdgcn_exp2f(m[gi] - mn);
-            m[gi] = mn;
-            l[gi] *= a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[gi][e] *= a;
-          }
-        }
-        float x[8];
+        for (int j = 0; j < NJ; ++j)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qf[j], sacc, 0,
+                                                         0, 0);
+        const int key0 = kt0 + t * kKT;
+        const bool full = key0 >= a0 && key0 + kKT <= c1 &&
+                          (key0 >= lo || key0 + kKT <= sk);
+        float sc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const unsigned vw = vr[r][e];
-          x[2 * e] = bf16_lo(vw);
-          x[2 * e + 1] = bf16_hi(vw);
+          sc[e] = sacc[e] * p.c;
+          if (!full) {
+            const int key = key0 + 4 * qg + e;
+            const bool ok = key >= a0 && key < c1 && (key >= lo || key < sk);
+            if (!ok) sc[e] = -INFINITY;
+          }
         }
+        const float mx =
+            quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        // move the running maximum only when a score exceeds it by more
+        // than 2^tau (any common shift of a row's scores is exact)
+        if (__builtin_amdgcn_ballot_w64(mx > M + kTau)) {
+          const float mn = fmaxf(M, mx);
+          const float alpha =
+              M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+          lsum *= alpha;
 #pragma unroll
-        for (int gi = 0; gi < GB; ++gi) {
-          const float pw = ok ? __builtin_amdgcn_exp2f(sc[gi] - m[gi]) : 0.f;
-          l[gi] += pw;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[gi][e] = fmaf(pw, x[e], o[gi][e]);
+          for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+          M = mn;
         }
+        const float mu = M == -INFINITY ? 0.f : M;
+        f32x4 pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pw[e] = __builtin_amdgcn_exp2f(sc[e] - mu);
+          lsum += pw[e];
+        }
+        const i16x4 pb =
+            __builtin_bit_cast(i16x4, __builtin_convertvector(pw, bf16x4));
+        // O^T += V^T . P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              va[db], pb, oacc[db], 0, 0, 0);
       }
-    }
+    });
   }
+  // the last loads (clamped rows past the chunk) land before the wave ends
+  wait_vm<0>();
 
-  // merge the row groups: first the GPW groups of each wavefront (lanes
-  // that differ in the row-group bits), then the wavefronts through LDS
+  const float lt = quad_sum(lsum);
+  if (n < nh) {
+    const size_t row = (size_t)(b * p.Hq + h0 + n) * p.nsplit + s;
+    const float inv = 1.f / lt;
 #pragma unroll
-  for (int gi = 0; gi < GB; ++gi) {
-    float mw = m[gi];
-    for (int x = LPK; x < 64; x <<= 1) mw = fmaxf(mw, __shfl_xor(mw, x));
-    const float a =
-        m[gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gi] - mw);
-    float lw = l[gi] * a;
-    for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float y = o[gi][e] * a;
-      for (int x = LPK; x < 64; x <<= 1) y += __shfl_xor(y, x);
-      o[gi][e] = y;
-    }
-    m[gi] = mw;
-    l[gi] = lw;
-  }
-  if (lane < LPK) {
-#pragma unroll
-    for (int gi = 0; gi < GB; ++gi)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_o[wave][gi * D + dch * 8 + e] = o[gi][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int gi = 0; gi < GB; ++gi) {
-      red_ml[wave][gi] = m[gi];
-      red_ml[wave][GB + gi] = l[gi];
-    }
-  }
-  __syncthreads();
-  for (int t = tid; t < nh * D; t += kThreads) {
-    const int gi = t / D;
-    const int d = t - gi * D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) mx = fmaxf(mx, red_ml[w][gi]);
-    float x = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const float mw = red_ml[w][gi];
-      const float a = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mx);
-      x = fmaf(a, red_o[w][t], x);
-      lsum = fmaf(a, red_ml[w][GB + gi], lsum);
-    }
-    const size_t row = (size_t)(b * p.Hq + h0 + gi) * p.nsplit + s;
-    p.ws_o[row * D + d] = x / lsum;
-    if (d == 0) p.ws_lse[row] = (mx + log2f(lsum)) * 0.69314718055994531f;
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * db + 4 * qg) =
+          oacc[db] * inv;
+    if (qg == 0) p.ws_lse[row] = (M + log2f(lt)) * 0.69314718055994531f;
   }
 }
 
@@ -384,27 +468,6 @@ int heads_per_block(int G) {
   return 1;
 }
 
-template <int D, int GB>
-void launch_split(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<D, GB>),
-                     dim3(p.B * p.Hkv * p.nhc, p.nsplit), dim3(kThreads), 0, st,
-                     p);
-}
-
-template <int D>
-void launch_split_d(const DecodeParams& p, hipStream_t st) {
-  switch (p.GB) {
-    case 1: launch_split<D, 1>(p, st); break;
-    case 2: launch_split<D, 2>(p, st); break;
-    case 3: launch_split<D, 3>(p, st); break;
-    case 4: launch_split<D, 4>(p, st); break;
-    case 5: launch_split<D, 5>(p, st); break;
-    case 6: launch_split<D, 6>(p, st); break;
-    case 7: launch_split<D, 7>(p, st); break;
-    default: launch_split<D, 8>(p, st); break;
-  }
-}
-
 }  // namespace
 
 int decode_max_keys() { return 65535 * kChunk; }
@@ -440,12 +503,13 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   p.ws_o = static_cast<float*>(ws);
   p.ws_lse = p.ws_o + rows * pr.d;
   const int ncomb = (pr.B * pr.Hq + kCombineWaves - 1) / kCombineWaves;
+  const dim3 grid(p.B * p.Hkv * p.nhc, p.nsplit);
   if (pr.d == 128) {
-    launch_split_d<128>(p, stream);
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64), 0, stream, p);
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(ncomb),
                        dim3(64 * kCombineWaves), 0, stream, p);
   } else {
-    launch_split_d<64>(p, stream);
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64), 0, stream, p);
     hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(ncomb),
                        dim3(64 * kCombineWaves), 0, stream, p);
   }
