@@ -498,7 +498,7 @@ def main():
                 "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for("decode"),
-                "kernels": "decode_split_kernel<128, 4> + "
+                "kernels": "decode_split_kernel<128> + "
                            "decode_combine_kernel<128>",
                 "algorithmic_bytes_per_launch": dbytes,
                 "avg_launch_ms": round(dec_avg, 5),

@@ -72,9 +72,8 @@ enum miattn_status {
   MIATTN_ERR_INVALID = -1,      /* null pointer, size <= 0, Hq % Hkv != 0,
                                    Nq > Nk, window, window_right or sinks
                                    < 0, non-finite scale,
-                                   pointer not 16-byte aligned, size overflow,
-                                   bf16 decode (Nq == 1) with
-                                   Nk > 33553920 */
+                                   pointer not 16-byte aligned, size overflow
+                                   (B*Hq*Nq or B*Hkv*Nk above 2^31 - 1) */
   MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; attn_fwd(_f32):
                                    window > 0 without
                                    causal */

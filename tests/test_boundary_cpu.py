@@ -138,14 +138,6 @@ def test_backward_rejected_on_host(over, code, msg):
     assert "attn_bwd" in err and msg in err, err
 
 
-def test_decode_key_limit_on_host():
-    # the bf16 decode grid covers at most 65535 splits of 512 keys; longer
-    # caches are refused before any HIP call
-    rc = call(mi.attn_fwd, good(Nq=1, Nk=65535 * 512 + 1))
-    assert rc == mi.MIATTN_ERR_INVALID
-    assert "at most 33553920" in mi.attn_last_error()
-
-
 def test_lse_may_be_null_and_still_validated():
     rc = call(mi.attn_fwd, good(lse=0, d=80))
     assert rc == mi.MIATTN_ERR_UNSUPPORTED

@@ -64,6 +64,11 @@ DECODE_CASES = [
     W("decode-g24-d128", 2, 48, 2, 1, 700, 128, "bf16", True, len_lo=300,
       len_hi=700),
     W("decode-g17-d128", 1, 17, 1, 1, 600, 128, "bf16", True),
+    # split sizes: small problems take 128-key splits; 160 (batch, K/V
+    # head) groups over 2048 keys take 256 (the full-size configurations
+    # cover 512 and 1024)
+    W("decode-chunk256", 20, 32, 8, 1, 2048, 128, "bf16", True, len_lo=1,
+      len_hi=2048),
 ]
 
 
@@ -74,7 +79,8 @@ def test_decode_small(w):
 
 
 def test_decode_chunk_boundaries():
-    """Valid lengths on and around the 512-key split boundaries."""
+    """Valid lengths on and around split boundaries (multiples of 128 keys:
+    the split size is a power of two from 128 up)."""
     w = W("decode-boundaries", 8, 4, 1, 1, 2048, 128, "bf16", True,
           len_lo=1, len_hi=2048)
     x = synth.make_inputs(w, 31)

@@ -138,10 +138,6 @@ int run_bf16(const char* fn, const void* q, const void* k, const void* v,
   hipError_t e;
   int rc;
   if (p.Nq == 1) {
-    if (p.Nk > miattn::decode_max_keys())
-      return fail(MIATTN_ERR_INVALID,
-                  "%s: decode supports at most %d cache rows (Nk=%d)", fn,
-                  miattn::decode_max_keys(), p.Nk);
     void* ws = nullptr;
     rc = workspace(miattn::decode_workspace_bytes(p), &ws);
     if (rc != MIATTN_OK) return rc;

@@ -7,7 +7,7 @@
 // j >= L_b - w; sink keys j < sinks always).
 //
 // Pass 1 (decode_split_kernel): grid = (batch, K/V head, head chunk) x split,
-//   one wavefront per workgroup.  A wavefront owns a chunk of kChunk keys of
+//   one wavefront per workgroup.  A wavefront owns a chunk of `chunk` keys of
 //   one (batch, K/V head) and the (up to 16) query heads of that group that
 //   share it, so each K and V byte is read from HBM once for all of them.
 //   The heads sharing a K/V head make the step a small matrix product, so it
@@ -30,6 +30,7 @@
 //   partition of the keys; written as bf16 o and fp32 lse.
 #include "kernels.h"
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -47,13 +48,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef MIATTN_DECODE_CHUNK
-#define MIATTN_DECODE_CHUNK 512
-#endif
 #ifndef MIATTN_DECODE_STAGES
 #define MIATTN_DECODE_STAGES 4
 #endif
-constexpr int kChunk = MIATTN_DECODE_CHUNK;    // keys per split
+// Keys per split: chosen per problem (decode_chunk), a power of two in
+// [kMinChunk, kMaxChunk] unless the grid's split limit asks for more.
+constexpr int kMinChunk = 128;
+constexpr int kMaxChunk = 1024;
+constexpr int kMaxSplits = 65535;  // grid y
+// Decode wavefronts the chip holds at once: 256 CUs, 5 per CU (LDS-bound).
+constexpr long long kSlots = 256 * 5;
 constexpr int kStages = MIATTN_DECODE_STAGES;  // LDS ring stages per wave
 constexpr int kKT = 16;          // keys per tile
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
@@ -70,7 +74,7 @@ struct DecodeParams {
   const int* seqlens;
   float* ws_o;    // [B, Hq, nsplit, D]
   float* ws_lse;  // [B, Hq, nsplit]
-  int B, Hq, Hkv, Nk, G, GB, nhc, window, sinks, nsplit;
+  int B, Hq, Hkv, Nk, G, GB, nhc, window, sinks, nsplit, chunk;
   float c;  // scale * log2(e)
 };
 
@@ -267,8 +271,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 
   int lo, L, sk;
   key_range(p, b, lo, L, sk);
-  const int c0 = s * kChunk;
-  const int c1 = min(c0 + kChunk, L);
+  const int c0 = s * p.chunk;
+  const int c1 = min(c0 + p.chunk, L);
   const int a0 = split_first_key(c0, c1, lo, sk);
   if (a0 >= c1) return;  // no allowed key here; the combine skips this split
   const int kt0 = c0 + (a0 - c0) / kKT * kKT;  // first key of the first tile
@@ -430,12 +434,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     return;
   }
   // the splits the split kernel wrote: those holding an allowed key
-  const int s0 = sk > 0 ? 0 : lo / kChunk;
-  const int s1 = (L + kChunk - 1) / kChunk;
+  const int s0 = sk > 0 ? 0 : lo / p.chunk;
+  const int s1 = (L + p.chunk - 1) / p.chunk;
   auto live = [&](int s) {
-    const int c0 = s * kChunk;
-    return split_first_key(c0, min(c0 + kChunk, L), lo, sk) <
-           min(c0 + kChunk, L);
+    const int c0 = s * p.chunk;
+    return split_first_key(c0, min(c0 + p.chunk, L), lo, sk) <
+           min(c0 + p.chunk, L);
   };
   float m = -INFINITY;
   for (int s = s0 + lane; s < s1; s += 64)
@@ -470,10 +474,27 @@ int heads_per_block(int G) {
 
 }  // namespace
 
-int decode_max_keys() { return 65535 * kChunk; }
+// The largest chunk that still gives every decode wavefront slot of the chip
+// a split (counting the keys a row may see: the valid length is only known
+// on the device, so Nk, or the window plus the sinks, bounds it), and no
+// smaller than the grid's split limit allows.
+int decode_chunk(const Problem& pr) {
+  const int G = pr.Hq / pr.Hkv;
+  const int GB = heads_per_block(G);
+  const long long groups = (long long)pr.B * pr.Hkv * ((G + GB - 1) / GB);
+  long long keys = pr.Nk;
+  if (pr.window > 0)
+    keys = std::min(keys, (long long)pr.window + std::max(pr.sinks, 0));
+  int chunk = kMaxChunk;
+  while (chunk > kMinChunk && groups * ((keys + chunk - 1) / chunk) < kSlots)
+    chunk /= 2;
+  while ((pr.Nk + (long long)chunk - 1) / chunk > kMaxSplits) chunk *= 2;
+  return chunk;
+}
 
 size_t decode_workspace_bytes(const Problem& pr) {
-  const size_t nsplit = (size_t)((pr.Nk + kChunk - 1) / kChunk);
+  const int chunk = decode_chunk(pr);
+  const size_t nsplit = (size_t)((pr.Nk + chunk - 1) / chunk);
   const size_t rows = (size_t)pr.B * pr.Hq * nsplit;
   return rows * (size_t)pr.d * sizeof(float) + rows * sizeof(float);
 }
@@ -497,7 +518,8 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   p.nhc = (p.G + p.GB - 1) / p.GB;
   p.window = pr.window;
   p.sinks = pr.sinks;
-  p.nsplit = (pr.Nk + kChunk - 1) / kChunk;
+  p.chunk = decode_chunk(pr);
+  p.nsplit = (pr.Nk + p.chunk - 1) / p.chunk;
   p.c = pr.scale * 1.4426950408889634f;
   const size_t rows = (size_t)pr.B * pr.Hq * p.nsplit;
   p.ws_o = static_cast<float*>(ws);

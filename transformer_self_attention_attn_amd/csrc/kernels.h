@@ -27,7 +27,6 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
 // Split-K bf16 decode (Nq == 1) and its log-sum-exp combine.  `ws` must hold
 // decode_workspace_bytes(p) bytes.
 size_t decode_workspace_bytes(const Problem& p);
-int decode_max_keys();  // largest Nk the decode grid can cover
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
                               void* o, float* lse, const Problem& p, void* ws,
                               hipStream_t stream);
