@@ -53,14 +53,15 @@
 //   maximum exceeds it by more than 2^8, which is exact arithmetic: the
 //   stored maximum is any common shift of the row's scores
 //   O^T[d][query] += V^T . P^T         A = V^T via transposing LDS reads,
-//                                      B = P^T (bf16) taken straight from
-//                                      the S^T accumulator
+//                                      B = P^T (bf16) converted from the
+//                                      S^T accumulator
 // Two-stage software pipeline: X(t) issues the S^T product of tile t+1 to the
 // matrix cores interleaved with the exponentials of tile t (and the tile
-// loads), Y(t) the V^T P^T product of tile t interleaved with the maximum of
-// tile t+1.  The two halves of the workgroup run half a tile apart (one takes
-// the workgroup barrier after Y, the other after X), so on every SIMD one
-// wavefront works through X while the other works through Y.
+// loads), Y(t) the V^T P^T product of tile t interleaved with the bf16
+// conversion and row sum of tile t and the maximum of tile t+1.  The two
+// halves of the workgroup run half a tile apart (one takes the workgroup
+// barrier after Y, the other after X), so on every SIMD one wavefront works
+// through X while the other works through Y.
 #include "kernels.h"
 
 #include <cmath>
@@ -447,10 +448,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // X(t): mask and maximum of tile t's scores `sc`, lazy rescale, and the
   // S^T product of tile t+1 (K slot SK) into `sn`, interleaved with tile t's
   // exponentials and with this wave's share of a tile load pair (K into slot
-  // SLK from kbi, V into slot SLV from vbi); P(t) leaves as bf16 in pb.
+  // SLK from kbi, V into slot SLV from vbi); the weights of tile t stay in
+  // `sc` (fp32) for Y(t).
   auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, const uint16_t* kbi,
                    const uint16_t* vbi, bool real_k, bool real_v, int t,
-                   f32x16(&sc)[2], f32x16(&sn)[2], bf16x8(&pb)[2][2]) {
+                   f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int SK = decltype(sk_c)::value;
     const int j0 = t * kKT;
     float mx = mx_pre;
@@ -501,7 +503,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     // keep the first operand reads ahead of the interleaved loop: the
     // scheduler fills the loop's LDS-read slots in program order
     __builtin_amdgcn_sched_barrier(0);
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int mb = i / C::KS, ks = i % C::KS;
@@ -519,7 +520,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         const int emb = el >> 4, er = el & 15;
         const float e = __builtin_amdgcn_exp2f(fmaf(sc[emb][er], p.c, -mu));
         sc[emb][er] = e;
-        ls[er & 3] += e;
       }
       // this step's loads, one per MFMA slot
       if (i < C::KLW)
@@ -533,22 +533,21 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       if (i < C::KLW + C::VLW)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
     }
-    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = sc[mb][8 * m + e];
-        pb[mb][m] = __builtin_convertvector(pv, bf16x8);
-      }
   };
 
-  // Y(t): O^T += V^T . P^T from V slot SV, interleaved with the maximum of
+  // Y(t): O^T += V^T . P^T from V slot SV, interleaved with the bf16
+  // conversion and row sum of this tile's weights `sc` and the maximum of
   // the next tile's scores `sn`.
-  auto tileY = [&](auto sv_c, const bf16x8(&pb)[2][2],
-                   const f32x16(&sn)[2]) {
+  auto tileY = [&](auto sv_c, const f32x16(&sc)[2], const f32x16(&sn)[2]) {
+    // P^T operands (bf16) converted from this tile's weights just ahead of
+    // the MFMAs that take them
+    auto cvt = [&](int mb, int m) {
+      f32x8 pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = sc[mb][8 * m + e];
+      return __builtin_convertvector(pv, bf16x8);
+    };
+    bf16x8 pcur = cvt(0, 0), pnext = pcur;
     // O^T += V^T . P^T; V operand reads run two MFMAs ahead.
     constexpr int NPV = 4 * C::DB;
     auto vread = [&](int i) {
@@ -568,6 +567,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       return a;
     };
     float mn2[2] = {-INFINITY, -INFINITY};
+    // row sum of this tile's weights in fp32 (lse needs the exact sum)
+    float l2[2] = {0.f, 0.f};
     bf16x8 va[5];
 #pragma unroll
     for (int i = 0; i < 4; ++i) va[i] = vread(i);
@@ -578,18 +579,27 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < NPV; ++i) {
       const int mb = i / (2 * C::DB), m = (i / C::DB) & 1, db = i % C::DB;
       if (i + 4 < NPV) va[(i + 4) % 5] = vread(i + 4);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 5], pb[mb][m],
+      if (db == 0 && i + C::DB < NPV)
+        pnext = cvt((i + C::DB) / (2 * C::DB), ((i + C::DB) / C::DB) & 1);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 5], pcur,
                                                          oacc[db], 0, 0, 0);
       mn2[0] = fmaxf(mn2[0], sn[(2 * i) >> 4][(2 * i) & 15]);
       mn2[1] = fmaxf(mn2[1], sn[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
+      // the 32 weights of this lane, 32 / NPV of them per MFMA slot
+#pragma unroll
+      for (int u = 0; u < 32 / NPV; ++u) {
+        const int el = i * (32 / NPV) + u;
+        l2[u & 1] += sc[el >> 4][el & 15];
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (db == C::DB - 1) pcur = pnext;
     }
     mx_pre = fmaxf(mn2[0], mn2[1]);
+    l += l2[0] + l2[1];
   };
 
   f32x16 sa[2], sb[2];
-  bf16x8 pb[2][2];
   // The two halves of the workgroup run half a tile apart: every wave runs
   // X(0) Y(0) X(1) Y(1) ... over the steps, but group 0 (waves 0 .. NW/2-1) takes
   // the workgroup barrier after each Y and group 1 after each X.  So on each
@@ -634,7 +644,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(),
             kg + (size_t)(whole_k ? rk : 0) * kKT * D,
             vg + (size_t)(whole_v ? rv : 0) * kKT * D, whole_k, whole_v, rt,
-            sc, sn, pb);
+            sc, sn);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
@@ -647,7 +657,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       wait_vmcnt(0);
       barrier_nofence();
     }
-    if (il) tileY(ic<K % 3>(), pb, sn);
+    if (il) tileY(ic<K % 3>(), sc, sn);
     if (!g1) {
       wait_vmcnt(0);
       barrier_nofence();
