@@ -28,10 +28,12 @@
 //
 // Data movement
 //   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
-//   loads (no register staging) into rings of two K and three V slots, each
-//   wave issuing its share of a tile's loads.  Rows past the valid
-//   length are loaded from a 16-byte block of zeros instead, so padded
-//   contents never enter LDS.  LDS rows are padded (K: +16 B, V: +64 B per
+//   buffer loads (no register staging) into rings of two K and three V
+//   slots, each wave issuing its share of a tile's loads.  Each tile is read
+//   through a buffer resource that starts at the tile and ends at the valid
+//   length, so rows past it read as zeros (padded contents never enter LDS)
+//   and a lane's offset within a tile is a constant: issuing a load costs
+//   scalar work only.  LDS rows are padded (K: +16 B, V: +64 B per
 //   row); with those strides every matrix-operand read below touches each LDS
 //   bank once, and every operand address is a per-lane base plus a
 //   compile-time offset.  K rows are stored in the order the 32x32 MFMA wants
@@ -67,6 +69,8 @@
 #include <cmath>
 #include <type_traits>
 
+#include "device_common.h"
+
 // Workgroup shape per head dimension, chosen by measurement on MI355X: d=128
 // runs 8 wavefronts (256 query rows share each K/V tile, one workgroup per
 // CU), d=64 runs 4 (128 rows, two per CU).
@@ -93,11 +97,6 @@ constexpr int kQW = 32;          // query rows per wavefront
 constexpr int kKT = 64;          // keys per tile
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
-
-// 16 zero bytes: the source of every direct-to-LDS load of a row past the
-// valid length.
-__device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u,
-                                                                     0u};
 
 template <int D, int NW>
 struct Cfg {
@@ -335,74 +334,62 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // ---- direct-to-LDS tile loads ---------------------------------------------
   // Wave-wide load i fills LDS bytes [i * 1024, +1024) of the tile: lane l
   // writes 16-byte slot i*64 + l, i.e. (row, chunk) of the padded row.  Loads
-  // are dealt round-robin to the waves; each lane's source offset within a
+  // are dealt round-robin to the waves; each lane's byte offset within a
   // tile is fixed, so it is computed once.  Pad chunks are never read and
-  // take the row's first chunk.  Only a tile that runs past the valid length
-  // takes the checked path, where such rows read the zero block.
-  unsigned koff[C::KLW], voff[C::VLW];
-  int krow[C::KLW], vrow[C::VLW];
+  // take the row's first chunk.  A tile is read through a buffer resource
+  // that starts at the tile and ends at the valid length: rows past it read
+  // as zeros, so padded contents never enter LDS.
+  unsigned kvo[C::KLW], vvo[C::VLW];
 #pragma unroll
   for (int m = 0; m < C::KLW; ++m) {
     const int slot16 = (wave + NW * m) * 64 + lane;
     const int r = slot16 / C::KSLOTS;
     const int c = slot16 - r * C::KSLOTS;
-    krow[m] = k_row_key(r);
-    koff[m] = krow[m] * D + (c < D / 8 ? c * 8 : 0);
+    kvo[m] = 2u * (k_row_key(r) * D + (c < D / 8 ? c * 8 : 0));
   }
 #pragma unroll
   for (int m = 0; m < C::VLW; ++m) {
     const int slot16 = (wave + NW * m) * 64 + lane;
     const int r = slot16 / C::VSLOTS;
     const int c = slot16 - r * C::VSLOTS;
-    vrow[m] = r;
-    voff[m] = r * D + (c < D / 8 ? c * 8 : 0);
+    vvo[m] = 2u * (r * D + (c < D / 8 ? c * 8 : 0));
   }
+  // resource of tile t of K or V (`live`: a tile of the plan; otherwise an
+  // empty range, whose reads touch no memory)
+  auto tile_rsrc = [&](const uint16_t* base, int t, bool live) {
+    const int rows = live ? max(0, min(kKT, L - t * kKT)) : 0;
+    return dev::rows_rsrc(live ? base + (size_t)t * kKT * D : base,
+                          rows * D * 2);
+  };
   // Interleaved loads (issued during X): every wave issues KLW + VLW of
-  // them per tile.  A wave without a load number m (uneven split), and every
-  // load of a step whose tiles take the checked path, reads the zero block
-  // into a 1 KB sink: its offset would point past the tile.
+  // them per tile.  A wave without a load number m (uneven split), and a step
+  // with no tile to load, writes into a 1 KB sink instead of the slot.
   __shared__ __attribute__((aligned(16))) uint16_t Sink[512];
-  auto dma_il = [&](const uint16_t* base, uint16_t* slot, bool real,
-                    unsigned off, int i, int nloads) {
+  auto dma_il = [&](miattn_i32x4 rs, uint16_t* slot, bool real, unsigned vo,
+                    int i, int nloads) {
     const bool ok = real && i < nloads;
-    __builtin_amdgcn_global_load_lds(
-        ok ? (const void*)(reinterpret_cast<const char*>(base) + 2u * off)
-           : (const void*)kZero16,
-        (lds_void*)(ok ? slot + i * 512 : Sink), 16, 0, 0);
+    miattn_buffer_load_lds(rs, (lds_void*)(ok ? slot + i * 512 : Sink), 16,
+                           (int)vo, 0, 0, 0);
   };
 
   auto dma_k = [&](auto slot_c, int t) {
-    constexpr int S = decltype(slot_c)::value;
-    const int j0 = t * kKT;
-    const uint16_t* base = kg + (size_t)j0 * D;
-    const bool whole = j0 + kKT <= L;
+    const miattn_i32x4 rs = tile_rsrc(kg, t, true);
 #pragma unroll
     for (int m = 0; m < C::KLW; ++m) {
       const int i = wave + NW * m;
-      if (i < C::KLOADS) {
-        const void* src = (whole || j0 + krow[m] < L)
-                              ? (const void*)(base + koff[m])
-                              : (const void*)kZero16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(kslot(slot_c) + i * 512),
-                                         16, 0, 0);
-      }
+      if (i < C::KLOADS)
+        miattn_buffer_load_lds(rs, (lds_void*)(kslot(slot_c) + i * 512), 16,
+                               (int)kvo[m], 0, 0, 0);
     }
   };
   auto dma_v = [&](auto slot_c, int t) {
-    constexpr int S = decltype(slot_c)::value;
-    const int j0 = t * kKT;
-    const uint16_t* base = vg + (size_t)j0 * D;
-    const bool whole = j0 + kKT <= L;
+    const miattn_i32x4 rs = tile_rsrc(vg, t, true);
 #pragma unroll
     for (int m = 0; m < C::VLW; ++m) {
       const int i = wave + NW * m;
-      if (i < C::VLOADS) {
-        const void* src = (whole || j0 + vrow[m] < L)
-                              ? (const void*)(base + voff[m])
-                              : (const void*)kZero16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(vslot(slot_c) + i * 512),
-                                         16, 0, 0);
-      }
+      if (i < C::VLOADS)
+        miattn_buffer_load_lds(rs, (lds_void*)(vslot(slot_c) + i * 512), 16,
+                               (int)vvo[m], 0, 0, 0);
     }
   };
 
@@ -448,10 +435,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // X(t): mask and maximum of tile t's scores `sc`, lazy rescale, and the
   // S^T product of tile t+1 (K slot SK) into `sn`, interleaved with tile t's
   // exponentials and with this wave's share of a tile load pair (K into slot
-  // SLK from kbi, V into slot SLV from vbi); the weights of tile t stay in
+  // SLK from resource krs, V into slot SLV from vrs); the weights of tile t
+  // stay in
   // `sc` (fp32) for Y(t).
-  auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, const uint16_t* kbi,
-                   const uint16_t* vbi, bool real_k, bool real_v, int t,
+  auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, miattn_i32x4 krs,
+                   miattn_i32x4 vrs, bool real_k, bool real_v, int t,
                    f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int SK = decltype(sk_c)::value;
     const int j0 = t * kKT;
@@ -523,9 +511,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       }
       // this step's loads, one per MFMA slot
       if (i < C::KLW)
-        dma_il(kbi, kslot(slk_c), real_k, koff[i], wave + NW * i, C::KLOADS);
+        dma_il(krs, kslot(slk_c), real_k, kvo[i], wave + NW * i, C::KLOADS);
       else if (i < C::KLW + C::VLW)
-        dma_il(vbi, vslot(slv_c), real_v, voff[i - C::KLW],
+        dma_il(vrs, vslot(slv_c), real_v, vvo[i - C::KLW],
                wave + NW * (i - C::KLW), C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
@@ -634,17 +622,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     constexpr int SLK = K % 2, SLV = (K + 1) % 3;
     const int tk = t + 2, tv = t + 1;  // steps whose tiles load now
     const int rt = tile_of(t), rk = tile_of(tk), rv = tile_of(tv);
-    const bool whole_k = tk < nt && (rk + 1) * kKT <= L;
-    const bool whole_v = tv < nt && (rv + 1) * kKT <= L;
+    const bool ld_k = tk < nt, ld_v = tv < nt;
     const bool il = wave_needs(rt);  // this wave's loads go inside X(t)
-    if (!(il && whole_v) && tv < nt) dma_v(ic<SLV>(), rv);
-    if (!(il && whole_k) && tk < nt) dma_k(ic<SLK>(), rk);
+    if (!il && ld_v) dma_v(ic<SLV>(), rv);
+    if (!il && ld_k) dma_k(ic<SLK>(), rk);
     if (il) {
-      // (a base is only dereferenced when its tile is whole)
-      tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(),
-            kg + (size_t)(whole_k ? rk : 0) * kKT * D,
-            vg + (size_t)(whole_v ? rv : 0) * kKT * D, whole_k, whole_v, rt,
-            sc, sn);
+      tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), tile_rsrc(kg, rk, ld_k),
+            tile_rsrc(vg, rv, ld_v), ld_k, ld_v, rt, sc, sn);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
