@@ -7,6 +7,8 @@ empty sequences, one valid key, window of one, N below one tile, GQA groups
 of 1, 2, 4, 7 and 16, negative and zero scale, NaN in the padding.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -311,3 +313,38 @@ def test_v_ones_gives_ones():
     live = torch.isfinite(lse)
     assert (o.float()[live] - 1).abs().max().item() <= 8e-3
     assert (o.float()[~live] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dominant_key_anywhere_in_a_tile(d):
+    """One key dominates every query's scores by about 200 (log2 units), far
+    past the lazy-rescale threshold and past what fp32 can hold as an
+    unshifted weight, so the running maximum must see it wherever it sits.
+    Batch b puts it at key pos[b]: the first 64-key tile and later ones, both
+    32-key halves of a tile.  The output must be that key's V row and lse its
+    score (the oracle's exact values)."""
+    import oracle
+    B, H, N = 4, 2, 256
+    pos = [40, 100, 200, 255]
+    g = torch.Generator().manual_seed(7)
+    u = torch.ones(d) / math.sqrt(d)
+    amp = math.sqrt(140.0 * math.sqrt(d))  # dominant score amp^2 / sqrt(d)
+    q = 0.1 * torch.randn(B, H, N, d, generator=g) + amp * u
+    k = 0.1 * torch.randn(B, H, N, d, generator=g)
+    for b, j in enumerate(pos):
+        k[b, :, j] = amp * u
+    v = torch.randn(B, H, N, d, generator=g)
+    qb, kb, vb = (t.to(torch.bfloat16) for t in (q, k, v))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gu.mi.attn(qb.to(gu.DEV), kb.to(gu.DEV), vb.to(gu.DEV),
+                        causal=False, scale=scale)
+    torch.cuda.synchronize()
+    go, gl = gu.host(o, lse)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    ro, rl = oracle.attention(f64(qb), f64(kb), f64(vb), scale=scale)
+    # the dominant scores really are far above the rest
+    s_dom = (f64(qb)[0, 0, 0] @ f64(kb)[0, 0, pos[0]]) * scale
+    assert s_dom * 1.4426950408889634 > 150
+    gu.compare(f"dominant-key-d{d}", "bf16", go, gl, ro, rl)
+    for b, j in enumerate(pos):
+        assert np.abs(go[b] - f64(vb)[b, :, j][:, None, :]).max() <= 2e-2

@@ -571,8 +571,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         pnext = cvt((i + C::DB) / (2 * C::DB), ((i + C::DB) / C::DB) & 1);
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 5], pcur,
                                                          oacc[db], 0, 0, 0);
-      mn2[0] = fmaxf(mn2[0], sn[(2 * i) >> 4][(2 * i) & 15]);
-      mn2[1] = fmaxf(mn2[1], sn[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
+      // the next tile's maximum, 32 / NPV of its 32 elements per MFMA slot
+#pragma unroll
+      for (int u = 0; u < 32 / NPV; ++u) {
+        const int el = i * (32 / NPV) + u;
+        mn2[u & 1] = fmaxf(mn2[u & 1], sn[el >> 4][el & 15]);
+      }
       // the 32 weights of this lane, 32 / NPV of them per MFMA slot
 #pragma unroll
       for (int u = 0; u < 32 / NPV; ++u) {
