@@ -154,6 +154,23 @@ CHUNK_SMALL = [
       len_hi=150),
     W("cross-fp32", 2, 2, 1, 40, 90, 128, "fp32", False, len_lo=1,
       len_hi=90),
+    # short chunks (query heads x rows of a K/V head within 16 columns) take
+    # the split-K matrix-core decode kernel; taller ones the prefill
+    W("chunk4-gqa4-d128-padded", 3, 8, 2, 4, 700, 128, "bf16", True,
+      len_lo=1, len_hi=700),
+    W("chunk16-mha-d64", 2, 4, 4, 16, 500, 64, "bf16", True),
+    W("chunk32-mha-d64-short", 3, 3, 3, 32, 1024, 64, "bf16", True,
+      len_lo=1, len_hi=1024),
+    W("chunk5-gqa7-d128-cross", 2, 14, 2, 5, 600, 128, "bf16", False,
+      len_lo=1, len_hi=600),
+    W("chunk3-win-sinks-d64", 2, 4, 2, 3, 900, 64, "bf16", True, window=50,
+      sinks=4, len_lo=1, len_hi=900),
+    W("chunk8-two-sided-d128", 2, 2, 2, 8, 300, 128, "bf16", False,
+      window=20, window_right=10, len_lo=30, len_hi=300),
+    W("chunk64-mha-d128", 2, 2, 2, 64, 777, 128, "bf16", True, len_lo=1,
+      len_hi=777),
+    W("chunk65-mha-d128", 2, 2, 2, 65, 777, 128, "bf16", True, len_lo=1,
+      len_hi=777),
 ]
 
 

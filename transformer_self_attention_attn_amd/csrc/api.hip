@@ -137,7 +137,7 @@ int run_bf16(const char* fn, const void* q, const void* k, const void* v,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   int rc;
-  if (p.Nq == 1) {
+  if (miattn::decode_takes(p)) {
     void* ws = nullptr;
     rc = workspace(miattn::decode_workspace_bytes(p), &ws);
     if (rc != MIATTN_OK) return rc;

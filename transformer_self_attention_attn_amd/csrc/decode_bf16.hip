@@ -61,7 +61,11 @@ constexpr long long kSlots = 256 * 5;
 constexpr int kStages = MIATTN_DECODE_STAGES;  // LDS ring stages per wave
 constexpr int kKT = 16;          // keys per tile
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
-constexpr int kMaxGB = 16;       // query heads per wavefront (MFMA columns)
+constexpr int kCols = 16;        // query columns per wavefront (MFMA N)
+// 1 < Nq < Nk goes to this kernel when its (head, row) columns fill one
+// wavefront per K/V head; taller chunks take the prefill kernel (a 32-row
+// chunk against 1024 keys, two column blocks, ran 10% slower here)
+constexpr int kMaxColumnBlocks = 1;
 constexpr int kCombineWaves = 4;  // (batch, head) rows per combine workgroup
 constexpr int kNonTemporal = 2;  // cache policy of the K/V loads: streamed
 
@@ -72,37 +76,70 @@ struct DecodeParams {
   uint16_t* o;
   float* lse;
   const int* seqlens;
-  float* ws_o;    // [B, Hq, nsplit, D]
-  float* ws_lse;  // [B, Hq, nsplit]
-  int B, Hq, Hkv, Nk, G, GB, nhc, window, sinks, nsplit, chunk;
+  float* ws_o;    // [B, Hq, Nq, nsplit, D]
+  float* ws_lse;  // [B, Hq, Nq, nsplit]
+  int B, Hq, Hkv, Nq, Nk, G, ncols, nhc, causal, window, window_right, sinks,
+      nsplit, chunk;
   float c;  // scale * log2(e)
 };
 
-__device__ inline void key_range(const DecodeParams& p, int b, int& lo,
-                                 int& L, int& sk) {
-  L = p.Nk;
+// Valid length of batch b.
+__device__ inline int valid_len(const DecodeParams& p, int b) {
+  int L = p.Nk;
   if (p.seqlens) {
     L = p.seqlens[b];
     L = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
   }
-  // the query sits at position L - 1: keys j <= L - 1 (causal or not, no key
-  // at or past L is valid); a window keeps L - 1 - j < w, i.e. j >= L - w
-  // (a right limit never removes a key here); sink keys j < sinks stay
-  lo = p.window > 0 ? max(0, L - p.window) : 0;
-  sk = min(p.sinks, L);
+  return L;
 }
 
-// Lowest allowed key of split s ([c0, c1) = its keys before the window and
-// sink rules): the split holds sink keys [c0, min(c1, sk)) and window keys
-// [max(c0, lo), c1); c1 (no allowed key) when both are empty.
-__device__ inline int split_first_key(int c0, int c1, int lo, int sk) {
-  if (c0 < sk && c0 < c1) return c0;
-  const int a = max(c0, lo);
-  return a < c1 ? a : c1;
+// Keys query row `row` (0 .. Nq-1) may see: the row sits at position
+// pos = L - Nq + row (the last Nq positions of the sequence; the one decode
+// row at L - 1).  Keys below hc (the valid length, and pos + 1 under the
+// causal mask); of those the window keys [lo, hw) (left limit pos - j < w,
+// right limit j - pos < wr, each off when 0) and the sink keys [0, sk).
+struct RowKeys {
+  int lo, hw, sk;
+};
+__device__ inline RowKeys row_keys(const DecodeParams& p, int L, int row) {
+  const int pos = L - p.Nq + row;
+  const int hc = max(0, p.causal ? min(L, pos + 1) : L);
+  RowKeys r;
+  r.hw = p.window_right > 0 ? max(0, min(hc, pos + p.window_right)) : hc;
+  r.lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  r.sk = min(p.sinks, hc);
+  return r;
+}
+__device__ inline bool key_ok(const RowKeys& r, int j) {
+  return j < r.sk || (j >= r.lo && j < r.hw);
+}
+// First allowed key of a row in [c0, c1) (c1 when none) and the end of its
+// allowed keys there (c0 when none).
+__device__ inline int split_first(const RowKeys& r, int c0, int c1) {
+  int f = c1;
+  if (c0 < min(r.sk, c1)) f = c0;
+  const int a = max(c0, r.lo), e = min(c1, r.hw);
+  if (a < e) f = min(f, a);
+  return f;
+}
+__device__ inline int split_end(const RowKeys& r, int c0, int c1) {
+  int e = c0;
+  if (c0 < min(r.sk, c1)) e = min(r.sk, c1);
+  const int a = max(c0, r.lo), w = min(c1, r.hw);
+  if (a < w) e = max(e, w);
+  return e;
 }
 
 __device__ inline float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ inline int wave_min_i(int x) {
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ inline int wave_max_i(int x) {
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m));
   return x;
 }
 
@@ -252,28 +289,36 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int hk = (blockIdx.x - b * nx) / p.nhc;
   const int hc = blockIdx.x - b * nx - hk * p.nhc;
   const int lane = threadIdx.x;
-  const int n = lane & 15;   // MFMA column: head (S^T, O^T), key row (K)
+  const int n = lane & 15;   // MFMA column (S^T, O^T), key row (K)
   const int qg = lane >> 4;  // lane group
-  const int h0 = hk * p.G + hc * p.GB;
-  const int nh = min(p.GB, p.G - hc * p.GB);
+  // column n of this block: query head hk*G + cl / Nq, row cl % Nq
+  const int cl = hc * 16 + n;
+  const bool cvalid = cl < p.ncols;
+  const int hh = cvalid ? cl / p.Nq : 0;
+  const int row = cvalid ? cl - hh * p.Nq : 0;
+  const size_t qrow = ((size_t)(b * p.Hq + hk * p.G + hh)) * p.Nq + row;
 
-  // Q^T operand: head n, columns 32j + 8qg .. +7 (zero for padding heads);
-  // issued before the valid length is known, the address does not depend on it
+  // Q^T operand: column n, features 32j + 8qg .. +7 (zero for padding
+  // columns); issued before the valid length is known, the address does not
+  // depend on it
   bf16x8 qf[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (n < nh)
-      raw = *reinterpret_cast<const u32x4*>(
-          p.q + (size_t)(b * p.Hq + h0 + n) * D + 32 * j + 8 * qg);
+    if (cvalid)
+      raw = *reinterpret_cast<const u32x4*>(p.q + qrow * D + 32 * j + 8 * qg);
     qf[j] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  int lo, L, sk;
-  key_range(p, b, lo, L, sk);
+  const int L = valid_len(p, b);
+  RowKeys rk = row_keys(p, L, row);
+  if (!cvalid) rk = {0, 0, 0};  // a padding column sees no key
+  // this split's keys [c0, c0 + chunk): the block's allowed keys there run
+  // from a0 to c1 (the union over its columns)
   const int c0 = s * p.chunk;
-  const int c1 = min(c0 + p.chunk, L);
-  const int a0 = split_first_key(c0, c1, lo, sk);
+  const int cend = c0 + p.chunk;
+  const int a0 = wave_min_i(split_first(rk, c0, cend));
+  const int c1 = wave_max_i(split_end(rk, c0, cend));
   if (a0 >= c1) return;  // no allowed key here; the combine skips this split
   const int kt0 = c0 + (a0 - c0) / kKT * kKT;  // first key of the first tile
   const int nt = (c1 - kt0 + kKT - 1) / kKT;   // tiles of this split
@@ -357,17 +402,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qf[j], sacc, 0,
                                                          0, 0);
         const int key0 = kt0 + t * kKT;
-        const bool full = key0 >= a0 && key0 + kKT <= c1 &&
-                          (key0 >= lo || key0 + kKT <= sk);
+        // no mask when every column allows all keys of the tile (padding
+        // columns count as allowing them: their results are never written)
+        const bool tile_ok = !cvalid ||
+                             (key0 >= rk.lo && key0 + kKT <= rk.hw) ||
+                             key0 + kKT <= rk.sk;
+        const bool full = __builtin_amdgcn_ballot_w64(!tile_ok) == 0;
         float sc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sc[e] = sacc[e] * p.c;
-          if (!full) {
-            const int key = key0 + 4 * qg + e;
-            const bool ok = key >= a0 && key < c1 && (key >= lo || key < sk);
-            if (!ok) sc[e] = -INFINITY;
-          }
+          if (!full && !key_ok(rk, key0 + 4 * qg + e)) sc[e] = -INFINITY;
         }
         const float mx =
             quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
@@ -403,43 +448,49 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   wait_vm<0>();
 
   const float lt = quad_sum(lsum);
-  if (n < nh) {
-    const size_t row = (size_t)(b * p.Hq + h0 + n) * p.nsplit + s;
-    const float inv = 1.f / lt;
+  if (cvalid) {
+    // a column with no allowed key in this split (possible when the block
+    // holds several rows) writes o = 0, lse = -inf; the combine reads only
+    // the splits that hold keys of its row
+    const size_t wrow = qrow * p.nsplit + s;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4*>(p.ws_o + row * D + 16 * db + 4 * qg) =
+      *reinterpret_cast<f32x4*>(p.ws_o + wrow * D + 16 * db + 4 * qg) =
           oacc[db] * inv;
-    if (qg == 0) p.ws_lse[row] = (M + log2f(lt)) * 0.69314718055994531f;
+    if (qg == 0)
+      p.ws_lse[wrow] =
+          lt > 0.f ? (M + log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
-// One wavefront per (batch, query head); lane l owns columns l*CPL..+CPL-1.
+// One wavefront per (batch, query head, row); lane l owns features
+// l*CPL .. +CPL-1.
 template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     DecodeParams p) {
   constexpr int CPL = D / 64;
   const int r = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
-  if (r >= p.B * p.Hq) return;  // wave-uniform
+  if (r >= p.B * p.Hq * p.Nq) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
-  const int b = r / p.Hq;
-  int lo, L, sk;
-  key_range(p, b, lo, L, sk);
+  const int b = r / (p.Hq * p.Nq);
+  const int row = r - (r / p.Nq) * p.Nq;
+  const int L = valid_len(p, b);
+  const RowKeys rk = row_keys(p, L, row);
   const size_t row0 = (size_t)r * p.nsplit;
   uint16_t* orow = p.o + (size_t)r * D + lane * CPL;
-  if (L <= lo && sk == 0) {  // no allowed key
+  if (rk.sk == 0 && rk.lo >= rk.hw) {  // no allowed key
 #pragma unroll
     for (int e = 0; e < CPL; ++e) orow[e] = 0;
     if (lane == 0 && p.lse) p.lse[r] = -INFINITY;
     return;
   }
-  // the splits the split kernel wrote: those holding an allowed key
-  const int s0 = sk > 0 ? 0 : lo / p.chunk;
-  const int s1 = (L + p.chunk - 1) / p.chunk;
+  // the splits holding keys of this row (their blocks wrote them)
+  const int s0 = rk.sk > 0 ? 0 : rk.lo / p.chunk;
+  const int s1 = (max(rk.hw, rk.sk) + p.chunk - 1) / p.chunk;
   auto live = [&](int s) {
     const int c0 = s * p.chunk;
-    return split_first_key(c0, min(c0 + p.chunk, L), lo, sk) <
-           min(c0 + p.chunk, L);
+    return split_first(rk, c0, c0 + p.chunk) < c0 + p.chunk;
   };
   float m = -INFINITY;
   for (int s = s0 + lane; s < s1; s += 64)
@@ -465,26 +516,25 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
   if (lane == 0 && p.lse) p.lse[r] = m + logf(wsum);
 }
 
-int heads_per_block(int G) {
-  if (G <= kMaxGB) return G;
-  for (int gb = kMaxGB; gb > 1; --gb)
-    if (G % gb == 0) return gb;
-  return 1;
+// Column blocks of one K/V head: its G query heads times Nq rows, 16 per
+// wavefront.
+long long column_blocks(const Problem& pr) {
+  const long long ncols = (long long)(pr.Hq / pr.Hkv) * pr.Nq;
+  return (ncols + kCols - 1) / kCols;
 }
 
 }  // namespace
 
 // The largest chunk that still gives every decode wavefront slot of the chip
 // a split (counting the keys a row may see: the valid length is only known
-// on the device, so Nk, or the window plus the sinks, bounds it), and no
-// smaller than the grid's split limit allows.
+// on the device, so Nk, or the window plus the sinks plus the rows, bounds
+// it), and no smaller than the grid's split limit allows.
 int decode_chunk(const Problem& pr) {
-  const int G = pr.Hq / pr.Hkv;
-  const int GB = heads_per_block(G);
-  const long long groups = (long long)pr.B * pr.Hkv * ((G + GB - 1) / GB);
+  const long long groups = (long long)pr.B * pr.Hkv * column_blocks(pr);
   long long keys = pr.Nk;
   if (pr.window > 0)
-    keys = std::min(keys, (long long)pr.window + std::max(pr.sinks, 0));
+    keys = std::min(keys, (long long)pr.window + std::max(pr.sinks, 0) +
+                              pr.Nq);
   int chunk = kMaxChunk;
   while (chunk > kMinChunk && groups * ((keys + chunk - 1) / chunk) < kSlots)
     chunk /= 2;
@@ -492,10 +542,15 @@ int decode_chunk(const Problem& pr) {
   return chunk;
 }
 
+bool decode_takes(const Problem& pr) {
+  return pr.Nq == 1 ||
+         (pr.Nq < pr.Nk && column_blocks(pr) <= kMaxColumnBlocks);
+}
+
 size_t decode_workspace_bytes(const Problem& pr) {
   const int chunk = decode_chunk(pr);
   const size_t nsplit = (size_t)((pr.Nk + chunk - 1) / chunk);
-  const size_t rows = (size_t)pr.B * pr.Hq * nsplit;
+  const size_t rows = (size_t)pr.B * pr.Hq * pr.Nq * nsplit;
   return rows * (size_t)pr.d * sizeof(float) + rows * sizeof(float);
 }
 
@@ -512,19 +567,24 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   p.B = pr.B;
   p.Hq = pr.Hq;
   p.Hkv = pr.Hkv;
+  p.Nq = pr.Nq;
   p.Nk = pr.Nk;
   p.G = pr.Hq / pr.Hkv;
-  p.GB = heads_per_block(p.G);
-  p.nhc = (p.G + p.GB - 1) / p.GB;
+  p.ncols = p.G * pr.Nq;
+  p.nhc = (int)column_blocks(pr);
+  p.causal = pr.causal;
   p.window = pr.window;
+  p.window_right = pr.window_right;
   p.sinks = pr.sinks;
   p.chunk = decode_chunk(pr);
   p.nsplit = (pr.Nk + p.chunk - 1) / p.chunk;
   p.c = pr.scale * 1.4426950408889634f;
-  const size_t rows = (size_t)pr.B * pr.Hq * p.nsplit;
+  const size_t rows = (size_t)pr.B * pr.Hq * pr.Nq * p.nsplit;
   p.ws_o = static_cast<float*>(ws);
   p.ws_lse = p.ws_o + rows * pr.d;
-  const int ncomb = (pr.B * pr.Hq + kCombineWaves - 1) / kCombineWaves;
+  const int ncomb =
+      (int)(((long long)pr.B * pr.Hq * pr.Nq + kCombineWaves - 1) /
+            kCombineWaves);
   const dim3 grid(p.B * p.Hkv * p.nhc, p.nsplit);
   if (pr.d == 128) {
     hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64), 0, stream, p);

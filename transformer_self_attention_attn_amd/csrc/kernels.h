@@ -24,8 +24,10 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
                                void* o, float* lse, const Problem& p,
                                hipStream_t stream);
 
-// Split-K bf16 decode (Nq == 1) and its log-sum-exp combine.  `ws` must hold
-// decode_workspace_bytes(p) bytes.
+// Split-K bf16 decode and its log-sum-exp combine: Nq == 1, and short chunks
+// 1 < Nq < Nk whose rows fit a few 16-column blocks (decode_takes).  `ws`
+// must hold decode_workspace_bytes(p) bytes.
+bool decode_takes(const Problem& p);
 size_t decode_workspace_bytes(const Problem& p);
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
                               void* o, float* lse, const Problem& p, void* ws,
