@@ -32,6 +32,7 @@ unchanged.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -80,12 +81,24 @@ def allowed_pairs(w, seqlens):
 
 
 def decode_bytes(w, seqlens):
-    keys = allowed_pairs(w, seqlens)  # one query row per (b, h): keys per b
+    """Algorithmic bytes of a decode-shaped call: every K/V row some query
+    row may see, read once for all the query heads and rows that share it
+    (for one row, or a causal chunk without a window, the last row sees them
+    all), plus q, o (bf16) and lse (fp32)."""
+    assert w.Nq == 1 or (w.causal and not w.window and not w.window_right
+                         and not w.sinks)
+    keys = allowed_pairs(dataclasses.replace(w, Nq=1), seqlens)  # per b
     kv = keys * w.Hkv * w.d * 2 * 2
-    q = w.B * w.Hq * w.d * 2
-    o = w.B * w.Hq * w.d * 2
-    lse = w.B * w.Hq * 4
+    q = w.B * w.Hq * w.Nq * w.d * 2
+    o = w.B * w.Hq * w.Nq * w.d * 2
+    lse = w.B * w.Hq * w.Nq * 4
     return kv + q + o + lse
+
+
+def decode_shaped(w):
+    """Calls the split-K decode kernel takes: one row, or a chunk whose
+    query heads x rows fit its 16 columns."""
+    return w.Nq == 1 or (w.Nq < w.Nk and (w.Hq // w.Hkv) * w.Nq <= 16)
 
 
 def trimmed(ms):
@@ -402,7 +415,8 @@ def main():
     # each; decode shapes in GB/s, the others in TFLOP/s
     extra, masks = {}, {}
     if not args.no_extra:
-        for name, seed in (("chunked-prefill-gqa", 17),
+        for name, seed in (("decode-chunk4-gqa", 22),
+                           ("chunked-prefill-gqa", 17),
                            ("cross-attention-padded", 18),
                            ("chunk32-gpt2-causal", 16),
                            ("local-window-bidirectional", 19),
@@ -422,7 +436,7 @@ def main():
                 run_w(i)
             prot = reps(run_w)
             sec = prot["trimmed_mean_ms"] * 1e-3
-            if w.Nq == 1:
+            if decode_shaped(w):
                 by = float(decode_bytes(w, xw["seqlens"]))
                 rec = {"value": round(by / sec / 1e9, 1), "unit": "GB/s",
                        "frac": round(by / sec / 1e9 / PEAK_HBM_GBS, 4),

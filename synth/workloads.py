@@ -60,6 +60,10 @@ WORKLOADS = (
     # one decode step against a padded KV cache
     Workload("decode-gqa", B=64, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128,
              dtype="bf16", causal=True, len_lo=2048, len_hi=8192),
+    # speculative decoding: 4 draft tokens checked against decode-gqa's
+    # caches in one call (G * Nq = 16 query columns per K/V head)
+    Workload("decode-chunk4-gqa", B=64, Hq=32, Hkv=8, Nq=4, Nk=8192, d=128,
+             dtype="bf16", causal=True, len_lo=2048, len_hi=8192),
     # -- Nq new rows against a longer key sequence (1 < Nq < Nk) --
     # 32 new tokens after a prompt (the generation setting of the SpAtten
     # review: 992 prompt tokens, 32 generated), GPT-2-small heads, padded cache

@@ -180,6 +180,7 @@ def test_chunk_and_cross_small(w):
 
 
 @pytest.mark.parametrize("name,seed", [
+    ("decode-chunk4-gqa", 22),
     ("chunk32-gpt2-causal", 16),
     ("chunked-prefill-gqa", 17),
     ("cross-attention-padded", 18),
