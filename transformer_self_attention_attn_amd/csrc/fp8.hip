@@ -54,6 +54,16 @@ namespace fp8_impl {
 
 using namespace dev;
 
+// max(x, x of the lane 32 apart) on the VALU: v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second,
+// both copies of x; two distinct registers, since the builtin given one
+// value twice was folded to a single result.
+__device__ inline float half_swap_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -469,10 +479,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
       }
   };
 
-  // softmax of tile t on its raw scores sc: W = P * vr as E4M3 in wb
-  // (bytes 0..15: keys 16g + r, 16..31: keys 32 + 16g + r), row sums in l
-  auto softmax = [&](int t, f32x16(&sc)[2], i32x8& wb) {
-    const float cs = crow * skh[t];
+  // softmax of tile t on its raw scores sc (skt, svt: the tile's K and V
+  // scales): W = P * vr as E4M3 in wb (bytes 0..15: keys 16g + r, 16..31:
+  // keys 32 + 16g + r), row sums in l
+  auto softmax = [&](int t, f32x16(&sc)[2], i32x8& wb, float skt,
+                     float svt) {
+    const float cs = crow * skt;
     if (!tile_full(t)) {
       const int j0 = t * kBlk;
 #pragma unroll
@@ -480,8 +492,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = j0 + mb * 32 + 16 * g + r;
-          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
-            sc[mb][r] = -INFINITY;
+          const bool off = (jj >= rk.hc) |
+                           (((jj < rk.lo) | (jj >= rk.hw)) & (jj >= rk.sk));
+          sc[mb][r] = off ? -INFINITY : sc[mb][r];
         }
     }
     float mr = -INFINITY;
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sc[mb][r]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32));
+    mr = half_swap_max(mr);
     const float mx = mr * cs;  // cs > 0: the largest score of the row
     if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
       const float mn = fmaxf(M, mx);
@@ -504,7 +517,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     }
     // w = 2^(acc cs - M) * vr = 2^(acc cs + (log2 vr - M)); the V ratio is
     // kept above 2^-100 so that a tile of zero V still counts in l
-    const float vr = fmaxf(svh[t] * inv_svm, 0x1p-100f);
+    const float vr = fmaxf(svt * inv_svm, 0x1p-100f);
     const float lv = __builtin_amdgcn_logf(vr) - ((M == -INFINITY) ? 0.f : M);
     float ls = 0.f;
 #pragma unroll
@@ -549,6 +562,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
   // Prologue: K(0), V(0), K(1) resident, S^T(0) formed.
   f32x16 sa[2], sb[2];
   if (nt > 0) {
+    // the scales of tile t + 1 are read in step t ahead of its tile loads:
+    // the wait for them is the end-of-step wait, not one in the softmax
+    // behind the loads in flight
+    float skc = skh[tile_of(0)], svc = svh[tile_of(0)];
     issue_k(ic<0>(), 0);
     issue_v(ic<0>(), 0);
     if (1 < nt) issue_k(ic<1>(), 1);
@@ -557,6 +574,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
     if (wave_needs(tile_of(0))) qk(ic<0>(), sa);
     auto step = [&](auto par_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
       constexpr int P = decltype(par_c)::value;
+      const float skt = skc, svt = svc;
+      if (t + 1 < nt) {
+        skc = skh[tile_of(t + 1)];
+        svc = svh[tile_of(t + 1)];
+      }
       if (t + 2 < nt) issue_k(ic<P>(), t + 2);
       if (t + 1 < nt) issue_v(ic<1 - P>(), t + 1);
       const int tt = tile_of(t);
@@ -564,15 +586,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fp8_kernel(Fp8Params p) {
       if (t + 1 < nt && wave_needs(tile_of(t + 1))) qk(ic<1 - P>(), sn);
       if (need) {
         i32x8 wb;
-        softmax(tt, sc, wb);
+        softmax(tt, sc, wb, skt, svt);
         pv(ic<P>(), wb);
       }
       wait_vm0();
       barrier_nofence();
     };
+    // the loop leaves from inside the pair rather than skipping its second
+    // step: the score buffers are dead after the loop, so the swap of roles
+    // costs no register copies at a join
     for (int t = 0; t < nt; t += 2) {
       step(ic<0>(), t, sa, sb);
-      if (t + 1 < nt) step(ic<1>(), t + 1, sb, sa);
+      if (t + 1 >= nt) break;
+      step(ic<1>(), t + 1, sb, sa);
     }
   }
 
