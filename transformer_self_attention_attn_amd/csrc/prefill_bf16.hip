@@ -631,8 +631,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     if (!il && ld_v) dma_v(ic<SLV>(), rv);
     if (!il && ld_k) dma_k(ic<SLK>(), rk);
     if (il) {
+      // X runs at a raised wave priority: where the two waves of a SIMD both
+      // have an instruction ready, the one in X (the exponentials, the
+      // longer phase) issues first
+      __builtin_amdgcn_s_setprio(1);
       tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), tile_rsrc(kg, rk, ld_k),
             tile_rsrc(vg, rv, ld_v), ld_k, ld_v, rt, sc, sn);
+      __builtin_amdgcn_s_setprio(0);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
