@@ -405,7 +405,7 @@ def main():
                "algorithmic_flop_per_launch": flops,
                "trimmed_mean_ms": round(prot8["trimmed_mean_ms"], 5),
                "quantize_ms": round(protq["trimmed_mean_ms"], 5),
-               "kernel": "attn_fp8_kernel<128, 8>",
+               "kernel": "attn_fp8_kernel<128, 4>",
                "workload": "gqa-causal-prefill, E4M3 codes with 64-row "
                            "block scales, Q and K rotated"}
         del z, fo8, fl8
@@ -498,7 +498,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for("prefill"),
-            "kernel": "prefill_kernel<128, 8>",
+            "kernel": "prefill_kernel<128, 4>",
             "algorithmic_flop_per_launch": flops,
             "avg_launch_ms": round(pre_avg, 5),
         },

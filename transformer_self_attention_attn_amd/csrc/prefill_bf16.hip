@@ -28,7 +28,7 @@
 //
 // Data movement
 //   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
-//   buffer loads (no register staging) into rings of two K and three V
+//   buffer loads (no register staging) into rings of two K and two V
 //   slots, each wave issuing its share of a tile's loads.  Each tile is read
 //   through a buffer resource that starts at the tile and ends at the valid
 //   length, so rows past it read as zeros (padded contents never enter LDS)
@@ -60,10 +60,11 @@
 // Two-stage software pipeline: X(t) issues the S^T product of tile t+1 to the
 // matrix cores interleaved with the exponentials of tile t (and the tile
 // loads), Y(t) the V^T P^T product of tile t interleaved with the bf16
-// conversion and row sum of tile t and the maximum of tile t+1.  The two
-// halves of the workgroup run half a tile apart (one takes the workgroup
-// barrier after Y, the other after X), so on every SIMD one wavefront works
-// through X while the other works through Y.
+// conversion and row sum of tile t and the maximum of tile t+1.  Two
+// workgroups share each CU (LDS and registers are sized for it), so every
+// SIMD runs wavefronts of two workgroups whose barriers are independent: they
+// drift apart and one wave's X overlaps the other's Y without any offset
+// imposed inside a workgroup.
 #include "kernels.h"
 
 #include <cmath>
@@ -71,11 +72,12 @@
 
 #include "device_common.h"
 
-// Workgroup shape per head dimension, chosen by measurement on MI355X: d=128
-// runs 8 wavefronts (256 query rows share each K/V tile, one workgroup per
-// CU), d=64 runs 4 (128 rows, two per CU).
+// Workgroup shape per head dimension, chosen by measurement on MI355X: both
+// run 4 wavefronts (128 query rows share each K/V tile) with at least two
+// workgroups per CU.  At d=128 one workgroup of 8 wavefronts per CU, its two
+// halves offset by half a tile, was 3-6% slower.
 #ifndef MIATTN_PREFILL_NW128
-#define MIATTN_PREFILL_NW128 8
+#define MIATTN_PREFILL_NW128 4
 #endif
 #ifndef MIATTN_PREFILL_NW64
 #define MIATTN_PREFILL_NW64 4
@@ -116,7 +118,9 @@ struct Cfg {
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static_assert(kKT * KSLOTS % 64 == 0 && kKT * VSLOTS % 64 == 0, "split");
   static_assert(KLW + VLW <= 4 * DB, "interleaved loads fit the PV product");
-  static_assert((2 * KTILE + 3 * VTILE) * 2 <= 160 * 1024, "LDS");
+  // two workgroups per CU: K and V rings and the 1 KB load sink of each fit
+  // in half of the 160 KB of LDS
+  static_assert((2 * KTILE + 2 * VTILE) * 2 + 1024 <= 80 * 1024, "LDS");
 };
 
 // Key held in row r of the K tile in LDS.  Rows are in MFMA row order: with
@@ -192,7 +196,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[C::VTILE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[C::VTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs2[C::VTILE];
   auto kslot = [&](auto s_c) -> uint16_t* {
     constexpr int S = decltype(s_c)::value;
     if constexpr (S == 0) return Ks0;
@@ -201,8 +204,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   auto vslot = [&](auto s_c) -> uint16_t* {
     constexpr int S = decltype(s_c)::value;
     if constexpr (S == 0) return Vs0;
-    else if constexpr (S == 1) return Vs1;
-    else return Vs2;
+    else return Vs1;
   };
 
   // ---- block -> (batch, head, query block) --------------------------------
@@ -592,18 +594,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   };
 
   f32x16 sa[2], sb[2];
-  // The two halves of the workgroup run half a tile apart: every wave runs
-  // X(0) Y(0) X(1) Y(1) ... over the steps, but group 0 (waves 0 .. NW/2-1) takes
-  // the workgroup barrier after each Y and group 1 after each X.  So on each
-  // SIMD one wave is in X (S^T MFMAs, exponentials, K reads, tile loads)
-  // while the other is in Y (PV MFMAs, V reads).  Between barriers j-1 and j
-  // (step t = j) group 0 runs X(t) Y(t) and group 1 runs Y(t-1) X(t); they
-  // read K(t+1), V(t) and V(t-1), and X(t) loads each wave's share of K(t+2)
-  // (over K(t), read by X(t-1)) and V(t+1) (over V(t-2), read by Y(t-2)).
-  // K and V of step t (tile tile_of(t)) live in K slot t % 2 and V slot
-  // t % 3.
-  const bool g1 = wave >= NW / 2;
-
+  // Step t runs X(t) Y(t), then waits for this wave's loads and takes the
+  // workgroup barrier.  X(t) reads K(t+1) and loads each wave's share of
+  // K(t+2) (over K(t), read by X(t-1)) and V(t+1) (over V(t-1), read by
+  // Y(t-1)); Y(t) reads V(t).  K and V of step t (tile tile_of(t)) live in
+  // slot t % 2.
   // ---- prologue: K(0), K(1), V(0) resident, S^T(0) formed ----------------
   if (nt > 0) {
     dma_k(ic<0>(), tile_of(0));
@@ -623,7 +618,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 
   auto step = [&](auto k_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int K = decltype(k_c)::value;
-    constexpr int SLK = K % 2, SLV = (K + 1) % 3;
+    constexpr int SLK = K % 2, SLV = (K + 1) % 2;
     const int tk = t + 2, tv = t + 1;  // steps whose tiles load now
     const int rt = tile_of(t), rk = tile_of(tk), rv = tile_of(tv);
     const bool ld_k = tk < nt, ld_v = tv < nt;
@@ -631,13 +626,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     if (!il && ld_v) dma_v(ic<SLV>(), rv);
     if (!il && ld_k) dma_k(ic<SLK>(), rk);
     if (il) {
-      // X runs at a raised wave priority: where the two waves of a SIMD both
-      // have an instruction ready, the one in X (the exponentials, the
-      // longer phase) issues first
-      __builtin_amdgcn_s_setprio(1);
       tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), tile_rsrc(kg, rk, ld_k),
             tile_rsrc(vg, rv, ld_v), ld_k, ld_v, rt, sc, sn);
-      __builtin_amdgcn_s_setprio(0);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
@@ -646,25 +636,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx_pre = fmaxf(mx_pre, sn[mb][r]);
     }
-    if (g1) {
-      wait_vmcnt(0);
-      barrier_nofence();
-    }
-    if (il) tileY(ic<K % 3>(), sc, sn);
-    if (!g1) {
-      wait_vmcnt(0);
-      barrier_nofence();
-    }
+    if (il) tileY(ic<K % 2>(), sc, sn);
+    wait_vmcnt(0);
+    barrier_nofence();
   };
-  // Unrolled by 6: every ring slot index is a compile-time constant and the
-  // two score buffers swap roles without copies.
-  for (int t = 0; t < nt; t += 6) {
+  // Unrolled by 2: every ring slot index is a compile-time constant and the
+  // two score buffers swap roles without copies (the loop leaves from inside
+  // the pair: the buffers are dead after it, so no join needs a copy).
+  for (int t = 0; t < nt; t += 2) {
     step(ic<0>(), t, sa, sb);
-    if (t + 1 < nt) step(ic<1>(), t + 1, sb, sa);
-    if (t + 2 < nt) step(ic<2>(), t + 2, sa, sb);
-    if (t + 3 < nt) step(ic<3>(), t + 3, sb, sa);
-    if (t + 4 < nt) step(ic<4>(), t + 4, sa, sb);
-    if (t + 5 < nt) step(ic<5>(), t + 5, sb, sa);
+    if (t + 1 >= nt) break;
+    step(ic<1>(), t + 1, sb, sa);
   }
 
   // ---- epilogue -----------------------------------------------------------
