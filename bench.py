@@ -375,7 +375,7 @@ def main():
                "algorithmic_flop_per_launch": bfl,
                "trimmed_mean_ms": round(protb["trimmed_mean_ms"], 5),
                "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128, 4> + "
-                          "bwd_dq_kernel<128, 8>",
+                          "bwd_dq_kernel<128, 4>",
                "workload": "gqa-causal-prefill, dO = N(0,1) seed [3, 1]"}
         del gout, gq, gk, gv
 

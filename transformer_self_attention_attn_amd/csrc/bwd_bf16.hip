@@ -597,7 +597,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
 // bwd_dq
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     BwdParams p) {
   using C = BCfg<D>;
   constexpr int QB = kWR * NW;  // query rows per workgroup
@@ -851,7 +851,10 @@ __global__ __launch_bounds__(64 * NW, (D == 128 ? 1 : 2)) void bwd_dq_kernel(
 }
 
 constexpr int kDkdvNW = 4;   // 128 keys per workgroup
-constexpr int kDqNW128 = 8;  // 256 rows per workgroup, two waves per SIMD
+// dQ: 128 rows per workgroup and two workgroups per CU (two waves per SIMD
+// from independent workgroups, which drift out of phase; one 8-wave
+// workgroup per CU was 5-10% slower at d=128)
+constexpr int kDqNW128 = 4;
 constexpr int kDqNW64 = 4;
 
 template <int D, int NWK, int NWQ>
