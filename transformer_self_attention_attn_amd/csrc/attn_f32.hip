@@ -104,10 +104,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
       l = l * alpha + wave_sum(pj);
       for (int c = 0; c < C; ++c) acc[c] *= alpha;
       const int nj = min(64, jhi - j0);
-      for (int jj = 0; jj < nj; ++jj) {
-        const float w = __shfl(pj, jj);
-        const float* vr = vb + (size_t)(j0 + jj) * D;
-        for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vr[lane + 64 * c], acc[c]);
+      // V rows in groups of 16, all loads of a group issued before its
+      // FMAs, so their latencies overlap instead of adding up
+      for (int jg = 0; jg < nj; jg += 16) {
+        float vv[16][C];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const bool in = jg + u < nj;
+          const float* vr = vb + (size_t)(j0 + (in ? jg + u : 0)) * D;
+#pragma unroll
+          for (int c = 0; c < C; ++c) vv[u][c] = vr[lane + 64 * c];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float w = __shfl(pj, jg + u);  // 0 past nj: pj = 0 there
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vv[u][c], acc[c]);
+        }
       }
       m = mn;
     }
