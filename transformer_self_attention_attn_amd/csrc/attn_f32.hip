@@ -85,6 +85,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
     for (int j0 = jlo; j0 < jhi; j0 += 64) {
       const int j = j0 + lane;
       const bool ok = j < jhi;
+      const int nj = min(64, jhi - j0);
+      // the tile's V rows, all loads issued ahead of the scores, so their
+      // latency overlaps the K loads' instead of adding to it (rows past nj
+      // repeat row j0 and are weighted by 0)
+      float vv[64][C];
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        const float* vr = vb + (size_t)(j0 + (u < nj ? u : 0)) * D;
+#pragma unroll
+        for (int c = 0; c < C; ++c) vv[u][c] = vr[lane + 64 * c];
+      }
       float s = -INFINITY;
       if (ok) {
         const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * D);
@@ -103,24 +114,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
       const float pj = ok ? expf(s - mn) : 0.f;
       l = l * alpha + wave_sum(pj);
       for (int c = 0; c < C; ++c) acc[c] *= alpha;
-      const int nj = min(64, jhi - j0);
-      // V rows in groups of 16, all loads of a group issued before its
-      // FMAs, so their latencies overlap instead of adding up
-      for (int jg = 0; jg < nj; jg += 16) {
-        float vv[16][C];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const bool in = jg + u < nj;
-          const float* vr = vb + (size_t)(j0 + (in ? jg + u : 0)) * D;
+      for (int u = 0; u < 64; ++u) {
+        const float w = __shfl(pj, u);  // 0 past nj: pj = 0 there
 #pragma unroll
-          for (int c = 0; c < C; ++c) vv[u][c] = vr[lane + 64 * c];
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float w = __shfl(pj, jg + u);  // 0 past nj: pj = 0 there
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vv[u][c], acc[c]);
-        }
+        for (int c = 0; c < C; ++c) acc[c] = fmaf(w, vv[u][c], acc[c]);
       }
       m = mn;
     }
