@@ -9,16 +9,24 @@ allowed query/key pair, both matrix products, masked pairs not counted); the
 decode step is reported in algorithmic HBM GB/s (valid K/V bytes + q + o +
 lse).  Per-launch durations come from HIP events recorded on the stream the
 kernels run on.  The fp64 CPU oracle is timed on a bounded sample of the
-prefill workload as a reported baseline.
+prefill workload as a reported baseline, with every core the process may use.
 
-Besides the step it times, back to back, the backward pass of the headline
-prefill and the 1 < Nq < Nk and local-window workloads (`--no-extra` skips
-them).
+Besides the step it times, launch by launch with the latency protocol of the
+SpAtten review (EVALUATION, latency: `--reps` repetitions, the largest and
+smallest 15% dropped, the middle 70% averaged): the two other bf16 prefill
+configurations (gpt2-small-causal-padded, sliding-window-causal), each against
+its own roofline; the backward pass and the FP8 forward of the headline
+prefill; and the 1 < Nq < Nk and local-window workloads (`--no-extra` skips
+all of these).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
                        [--no-cpu-baseline] [--no-extra] [--copy-probe MIB]
+       python bench.py --only WORKLOAD [--seed S] [--reps R] [--warmup W]
        python bench.py --fold-traffic FETCH.csv WRITE.csv
-Prints one JSON line.
+       python bench.py --fold-counters COUNTERS.csv
+Prints one JSON line.  `--only` runs one workload's forward call alone
+(`backward` runs the headline's backward pass): the form used under
+rocprofv3, so a profile holds that workload's kernels only.
 
 HBM traffic: two rocprofv3 counter runs of a short bench with `--no-extra
 --copy-probe 1024` (so that the only launches of the kernels are the step's;
@@ -187,50 +195,219 @@ def fold_traffic(fetch_csv, write_csv, copy_bytes):
     return rec
 
 
+def fold_counters(csv_path, kernel_substr="", simds=1024, dies=8):
+    """Per-kernel averages over the dispatches of a rocprofv3 counter CSV
+    (rocprofv3 sums each counter over its hardware instances), with the
+    derived ratios: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over (SIMDs x
+    GRBM_GUI_ACTIVE per die; GRBM_GUI_ACTIVE is counted on each of the 8
+    dies), and instructions per MFMA.  Returns {kernel: {counter: value}}."""
+    import collections
+    import csv
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel_substr not in row["Kernel_Name"]:
+                continue
+            d = int(row["Dispatch_Id"])
+            per[d][row["Counter_Name"]] += float(row["Counter_Value"])
+            names[d] = row["Kernel_Name"]
+    out = {}
+    for name in sorted(set(names.values())):
+        ds = [d for d in per if names[d] == name]
+        avg = {c: sum(per[d].get(c, 0.0) for d in ds) / len(ds)
+               for c in sorted({c for d in ds for c in per[d]})}
+        avg["dispatches"] = len(ds)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+            avg["mfma_busy_pct"] = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (
+                simds * avg["GRBM_GUI_ACTIVE"] / dies)
+        if avg.get("SQ_INSTS_MFMA"):
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS"):
+                if c in avg:
+                    avg[c + "_per_mfma"] = avg[c] / avg["SQ_INSTS_MFMA"]
+        out[name] = avg
+    return out
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, x, budget_s=20.0):
     """Times the fp64 oracle (as it stands) on whole (batch, head) slices of
     the prefill workload, in order, until about `budget_s` seconds of CPU
-    work are done; reports algorithmic TFLOP/s of that sample."""
+    work are done; reports algorithmic TFLOP/s of that sample.  Every core
+    the process may use (its affinity set) runs the oracle's BLAS calls."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()]
-                      or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+        limiter, threads = None, None
     q32, k32, v32 = x["q32"], x["k32"], x["v32"]
     done = 0
     t_total = 0.0
     per_head_pairs = allowed_pairs(w.with_(B=1), None)
     g = w.Hq // w.Hkv
-    while t_total < budget_s and done < w.B * w.Hq:
-        b, h = divmod(done, w.Hq)
-        hk = h // g
-        t0 = time.perf_counter()
-        oracle.attention(q32[b:b + 1, h:h + 1], k32[b:b + 1, hk:hk + 1],
-                         v32[b:b + 1, hk:hk + 1], scale=w.scale,
-                         causal=w.causal, window=w.window, seqlens=None)
-        t_total += time.perf_counter() - t0
-        done += 1
+    try:
+        while t_total < budget_s and done < w.B * w.Hq:
+            b, h = divmod(done, w.Hq)
+            hk = h // g
+            t0 = time.perf_counter()
+            oracle.attention(q32[b:b + 1, h:h + 1], k32[b:b + 1, hk:hk + 1],
+                             v32[b:b + 1, hk:hk + 1], scale=w.scale,
+                             causal=w.causal, window=w.window, seqlens=None)
+            t_total += time.perf_counter() - t0
+            done += 1
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
     flops = 4.0 * w.d * per_head_pairs * done
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": cores, "blas_threads": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": (f"{done} of {w.B * w.Hq} (batch, head) slices of "
                        f"{w.name}, all {w.Nq} query rows each, "
                        f"{t_total:.1f} s of fp64 NumPy"),
             "seconds": round(t_total, 2)}
 
 
+def prefill_roofline(w, seqlens, sec):
+    """Roofline record of a bf16 prefill-shaped call taking `sec` seconds:
+    the bound is whichever of the MFMA time (algorithmic FLOPs at the dense
+    bf16 peak) and the HBM time (compulsory bytes at the HBM peak) is
+    longer; compulsory bytes are q and o of the live rows, k and v of the
+    valid keys (bf16) and lse (fp32)."""
+    pairs = allowed_pairs(w, seqlens) * w.Hq
+    flops = 4.0 * w.d * pairs
+    lens = [w.Nk] * w.B if seqlens is None else \
+        [int(min(max(v, 0), w.Nk)) for v in seqlens]
+    live_q = sum(L if w.Nq == w.Nk else w.Nq for L in lens)
+    byts = float(live_q * w.Hq * (2 * w.d * 2 + 4)
+                 + sum(lens) * w.Hkv * 2 * w.d * 2)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
+        ach = byts / sec / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": byts,
+                "algorithmic_flop_per_launch": flops,
+                "tflops": round(flops / sec / 1e12, 2)}
+    ach = flops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": byts}
+
+
+def shape_str(w):
+    return (f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} "
+            f"d={w.d} causal={w.causal}"
+            + (f" window={w.window}" if w.window else "")
+            + (f" window_right={w.window_right}" if w.window_right else "")
+            + (f" sinks={w.sinks}" if w.sinks else "")
+            + (f" L~U[{w.len_lo},{w.len_hi}]" if w.padded else ""))
+
+
+def run_only(args):
+    """One workload's forward call (or the headline's backward pass) alone:
+    warmup, then `reps` launches with HIP events around each; one JSON line
+    with the trimmed mean.  Meant to run under rocprofv3."""
+    import torch
+    import synth
+    import transformer_self_attention_attn_amd as mi
+    mi.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    name = args.only
+    bwd = name == "backward"
+    w = synth.by_name("gqa-causal-prefill" if bwd else name)
+    seed = args.seed if args.seed is not None else SEEDS.get(w.name, 0)
+    x = synth.make_inputs(w, seed)
+    sl = None if x["seqlens"] is None else \
+        torch.from_numpy(x["seqlens"]).to(dev)
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def fwd(i):
+        mi.attn(q, k, v, causal=w.causal, window=w.window, seqlens=sl,
+                out=o, lse=lse, window_right=w.window_right, sinks=w.sinks)
+    fn = fwd
+    if bwd:
+        fwd(0)
+        gout = synth.make_dout(w, seed)[0].to(dev)
+        gq, gk, gv = (torch.empty_like(q), torch.empty_like(k),
+                      torch.empty_like(v))
+
+        def fn(i):
+            rc = mi.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             o.data_ptr(), gout.data_ptr(), lse.data_ptr(),
+                             gq.data_ptr(), gk.data_ptr(), gv.data_ptr(),
+                             w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.scale,
+                             int(w.causal), w.window, w.window_right,
+                             w.sinks, 0 if sl is None else sl.data_ptr(),
+                             stream.cuda_stream)
+            assert rc == mi.MIATTN_OK, mi.attn_last_error()
+    for i in range(args.warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(args.reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    prot = trimmed([a.elapsed_time(b) for a, b in ev])
+    rec = {"only": name, "seed": seed, "shape": shape_str(w), **prot}
+    if not bwd and not decode_shaped(w):
+        rec["roofline"] = prefill_roofline(w, x["seqlens"],
+                                           prot["trimmed_mean_ms"] * 1e-3)
+    print(json.dumps(rec), flush=True)
+
+
+# seeds of the workloads' headline inputs (the first of each one's test seeds)
+SEEDS = {"fp32-single-head": 1, "gpt2-small-causal-padded": 2,
+         "gqa-causal-prefill": 3, "sliding-window-causal": 4,
+         "decode-gqa": 5, "chunk32-gpt2-causal": 16,
+         "chunked-prefill-gqa": 17, "cross-attention-padded": 18,
+         "local-window-bidirectional": 19, "sliding-window-sinks": 20,
+         "decode-window-sinks": 21, "decode-chunk4-gqa": 22}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--reps", type=int, default=200,
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--reps", type=int, default=1000,
                     help="repetitions of the trimmed-mean latency protocol")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the Nq < Nk workloads (chunks, cross-attention)")
+                    help="time the step only (no other configurations, "
+                         "backward, FP8, chunks or local windows)")
+    ap.add_argument("--only", metavar="WORKLOAD",
+                    help="run one workload (or `backward`) alone and exit")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="input seed for --only (default: the workload's)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device to "
                          "device three times (counter calibration)")
@@ -238,7 +415,13 @@ def main():
                     help="fold two counter CSVs into profiles/traffic.json")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of the probe copy the CSVs hold")
+    ap.add_argument("--fold-counters", metavar="CSV",
+                    help="print per-kernel counter averages of a rocprofv3 "
+                         "counter_collection.csv as JSON")
     args = ap.parse_args()
+    if args.fold_counters:
+        print(json.dumps(fold_counters(args.fold_counters), indent=1))
+        return
     if args.fold_traffic:
         rec = fold_traffic(*args.fold_traffic, args.copy_mib << 20)
         with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
@@ -250,8 +433,10 @@ def main():
               f"{args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        run_only(args)
+        return
 
-    import numpy as np
     import torch
     import synth
     import transformer_self_attention_attn_amd as mi
@@ -259,12 +444,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
     wp = synth.by_name("gqa-causal-prefill")
     wd = synth.by_name("decode-gqa")
     wf = synth.by_name("fp32-single-head")
-    xp = synth.make_inputs(wp, 3)
-    xd = synth.make_inputs(wd, 5)
-    xf = synth.make_inputs(wf, 1)
+    xp = synth.make_inputs(wp, SEEDS[wp.name])
+    xd = synth.make_inputs(wd, SEEDS[wd.name])
+    xf = synth.make_inputs(wf, SEEDS[wf.name])
 
     def dev_in(x):
         sl = None
@@ -331,7 +517,7 @@ def main():
     tflops = flops / (pre_avg * 1e-3) / 1e12
     gbs = dbytes / (dec_avg * 1e-3) / 1e9
 
-    # latency protocol: R single-kernel repetitions each, trimmed mean
+    # latency protocol: R single-call repetitions each, trimmed mean
     def reps(fn):
         out = []
         for i in range(args.reps):
@@ -347,13 +533,37 @@ def main():
     proto_p = reps(lambda i: prefill())
     proto_d = reps(decode)
 
+    # the two other bf16 prefill configurations, each against its roofline
+    configs = {}
+    if not args.no_extra:
+        for name in ("gpt2-small-causal-padded", "sliding-window-causal"):
+            w = synth.by_name(name)
+            xw = synth.make_inputs(w, SEEDS[name])
+            Xw = dev_in(xw)
+            ow = torch.empty_like(Xw[0])
+            lw = torch.empty(Xw[0].shape[:3], dtype=torch.float32,
+                             device=dev)
+
+            def run_c(i, w=w, Xw=Xw, ow=ow, lw=lw):
+                mi.attn(Xw[0], Xw[1], Xw[2], causal=w.causal,
+                        window=w.window, seqlens=Xw[3], out=ow, lse=lw)
+            for i in range(args.warmup):
+                run_c(i)
+            prot = reps(run_c)
+            rec = prefill_roofline(w, xw["seqlens"],
+                                   prot["trimmed_mean_ms"] * 1e-3)
+            rec.update(kernel=f"prefill_kernel<{w.d}>", seed=SEEDS[name],
+                       shape=shape_str(w), latency_protocol=prot)
+            configs[name] = rec
+            del Xw, ow, lw
+
     # backward pass of the headline prefill: dQ, dK, dV from the forward's
     # o and lse and a seeded dO (all three kernels of one attn_bwd call);
     # algorithmic FLOPs 2.5x the forward's (10*d per allowed pair)
     bwd = None
     if not args.no_extra:
         prefill()
-        gout = synth.make_dout(wp, 3)[0].to(dev)
+        gout = synth.make_dout(wp, SEEDS[wp.name])[0].to(dev)
         gq, gk, gv = (torch.empty_like(P[0]), torch.empty_like(P[1]),
                       torch.empty_like(P[2]))
         sptr = stream.cuda_stream
@@ -374,8 +584,7 @@ def main():
                "frac": round(btf / PEAK_BF16_TFLOPS, 4),
                "algorithmic_flop_per_launch": bfl,
                "trimmed_mean_ms": round(protb["trimmed_mean_ms"], 5),
-               "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128, 4> + "
-                          "bwd_dq_kernel<128, 4>",
+               "kernels": "bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel",
                "workload": "gqa-causal-prefill, dO = N(0,1) seed [3, 1]"}
         del gout, gq, gk, gv
 
@@ -415,15 +624,12 @@ def main():
     # each; decode shapes in GB/s, the others in TFLOP/s
     extra, masks = {}, {}
     if not args.no_extra:
-        for name, seed in (("decode-chunk4-gqa", 22),
-                           ("chunked-prefill-gqa", 17),
-                           ("cross-attention-padded", 18),
-                           ("chunk32-gpt2-causal", 16),
-                           ("local-window-bidirectional", 19),
-                           ("sliding-window-sinks", 20),
-                           ("decode-window-sinks", 21)):
+        for name in ("decode-chunk4-gqa", "chunked-prefill-gqa",
+                     "cross-attention-padded", "chunk32-gpt2-causal",
+                     "local-window-bidirectional", "sliding-window-sinks",
+                     "decode-window-sinks"):
             w = synth.by_name(name)
-            xw = synth.make_inputs(w, seed)
+            xw = synth.make_inputs(w, SEEDS[name])
             Xw = dev_in(xw)
             ow = torch.empty_like(Xw[0])
             lw = torch.empty(Xw[0].shape[:3], dtype=torch.float32, device=dev)
@@ -447,14 +653,7 @@ def main():
                        "frac": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
                        "algorithmic_flop_per_launch": fl}
             rec["trimmed_mean_ms"] = round(prot["trimmed_mean_ms"], 5)
-            rec["shape"] = (
-                f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} "
-                f"d={w.d} causal={w.causal}"
-                + (f" window={w.window}" if w.window else "")
-                + (f" window_right={w.window_right}" if w.window_right
-                   else "")
-                + (f" sinks={w.sinks}" if w.sinks else "")
-                + (f" L~U[{w.len_lo},{w.len_hi}]" if w.padded else ""))
+            rec["shape"] = shape_str(w)
             local = w.window or w.window_right or w.sinks
             (masks if local else extra)[name] = rec
             del Xw, ow, lw
@@ -491,6 +690,9 @@ def main():
             "seq_len": wp.Nq,
             "parallelism": "none (one GPU)",
         },
+        "device": {"name": props.name,
+                   "arch": getattr(props, "gcnArchName", None),
+                   "compute_units": props.multi_processor_count},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -498,7 +700,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for("prefill"),
-            "kernel": "prefill_kernel<128, 4>",
+            "kernel": "prefill_kernel<128>",
             "algorithmic_flop_per_launch": flops,
             "avg_launch_ms": round(pre_avg, 5),
         },
@@ -521,6 +723,8 @@ def main():
         "fp32_case_avg_ms": round(sum(f32_ms) / K, 5),
         "latency_protocol": {"prefill": proto_p, "decode": proto_d},
     }
+    if configs:
+        line["configs"] = configs
     if bwd:
         line["backward"] = bwd
     if fp8:

@@ -48,12 +48,22 @@
  *
  * Ownership: every pointer is a device pointer owned by the caller; the
  * library writes only its outputs (o and lse; dq, dk and dv for attn_bwd).
- * The decode path (Nq == 1) and attn_bwd use a library-owned device
- * workspace per device, allocated on first use (and grown when a larger
- * problem arrives) and released by attn_release().  Calls are asynchronous on
- * `stream` (a hipStream_t; NULL = the null stream) and never synchronise.
- * Two concurrent decode or backward calls on one device share the workspace
- * and must be ordered by the caller (same stream).
+ *
+ * Workspace: three paths keep partial results in a library-owned device
+ * buffer, one per device: the decode step (Nq == 1), short chunks
+ * (1 < Nq < Nk with (Hq / Hkv) * Nq <= 16, which run on the decode
+ * kernels), and attn_bwd.  The buffer is allocated on a path's first call
+ * and grown when a larger problem arrives; attn_release() frees it.
+ * Growth calls hipFree and hipMalloc, and hipFree waits for the whole device
+ * to finish: a call that grows the workspace synchronises the device.  Every
+ * other call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream) and never synchronises; a caller that must not synchronise makes
+ * one call of its largest size first.  The
+ * library holds a lock from the size check through the launch, so calls
+ * from several host threads never free a buffer a queued launch still
+ * names; but all workspace users on one device share the one buffer, so
+ * their kernels must not overlap: issue them on one stream, or order the
+ * streams.
  *
  * Errors: the return value is a status.  Argument checks run on the host
  * before any HIP call, so they are testable without a GPU.  No call aborts or
@@ -75,8 +85,10 @@ enum miattn_status {
                                    pointer not 16-byte aligned, size overflow
                                    (B*Hq*Nq or B*Hkv*Nk above 2^31 - 1) */
   MIATTN_ERR_UNSUPPORTED = -2,  /* d not in {64, 128}; attn_fwd(_f32):
-                                   window > 0 without
-                                   causal */
+                                   window > 0 without causal; attn_bwd and
+                                   the FP8 calls: one sequence (Nq rows, or
+                                   Nk rows padded to 64, of d bf16) spanning
+                                   2^31 bytes or more */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
   MIATTN_ERR_NOMEM = -4         /* the workspace could not be grown */
 };
@@ -188,7 +200,8 @@ int attn_fwd_fp8(const void* q8, const float* sq, const void* k8,
 const char* attn_last_error(void);
 
 /* Frees the library-owned workspace on every device that has one.
- * The caller must ensure no decode call is still running. */
+ * The caller must ensure no call that uses it (see Workspace above) is
+ * still running. */
 void attn_release(void);
 
 #ifdef __cplusplus

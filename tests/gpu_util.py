@@ -144,5 +144,27 @@ def check_sampled(name, w, seed, x=None, o_lse=None):
     return compare(name, w.dtype, go, gl, ro, rl, vmag=w.amp)
 
 
+def check_whole_slices(name, w, seed, slices):
+    """Full-size run; the listed (batch, head) slices compared row by row
+    with the oracle on that slice alone (every query row, every key)."""
+    say(f"[gpu] {name} (full size, whole slices {slices}) seed={seed}")
+    x = synth.make_inputs(w, seed)
+    o, lse = run_gpu(w, x)
+    g = w.Hq // w.Hkv
+    out = []
+    for b, h in slices:
+        hk = h // g
+        sl = None if x["seqlens"] is None else x["seqlens"][b:b + 1]
+        ro, rl = oracle.attention(
+            x["q32"][b:b + 1, h:h + 1], x["k32"][b:b + 1, hk:hk + 1],
+            x["v32"][b:b + 1, hk:hk + 1], scale=w.scale, causal=w.causal,
+            window=w.window, seqlens=sl, window_right=w.window_right,
+            sinks=w.sinks)
+        go, gl = host(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1])
+        out.append(compare(f"{name} b={b} h={h}", w.dtype, go, gl, ro, rl,
+                           vmag=w.amp))
+    return out
+
+
 def finite_scale(d):
     return 1.0 / math.sqrt(d)

@@ -228,10 +228,86 @@ def check_quantize_all(fp8, seed=65):
     assert err.max() < 0.1 and err.mean() < 0.02, (err.max(), err.mean())
 
 
+def _bf16(x):
+    """float32 values rounded to bfloat16 (nearest even), kept in float32."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.bfloat16).to(torch.float32).numpy()
+
+
+def check_fwht_f32_against_exact_rotation(fp8, seed=66):
+    """The float32 butterflies against the exact rotation, independently of
+    any kernel.
+
+    Exact: for bfloat16 inputs (8 significant bits) at d <= 128, x D H is a
+    sum of at most 128 signed bf16 values; scaled by a power of two they are
+    integers far below 2^53, so a float64 matrix product holds them exactly
+    (checked here against an int64 product).
+    Error bound: the float32 transform runs log2(d) butterfly stages, each
+    rounding once (unit roundoff u = 2^-24) a value bounded by sum_i |x_i|,
+    so |fwht_f32(x) - x H| <= log2(d) u sum_i |x_i| (to first order).
+    Code decisions: with the float32 path's block multiplier, a code of the
+    float32 value may differ from the code of the exact value only where the
+    exact scaled value lies within that error (plus the float32 product's
+    own rounding) of a midpoint between two E4M3 values.  Such codes are
+    counted and bounded.  On these inputs the float32 values carry any
+    rounding in 1-3% of elements, at most 0.14 of the bound, and no code of
+    the 786432 differs from the exact rotation's."""
+    rng = np.random.default_rng(seed)
+    mids = (fp8._POS[:-1] + fp8._POS[1:]) / 2.0
+    u = 2.0 ** -24
+    changed_total = 0
+    codes_total = 0
+    for d in (64, 128):
+        n = 4096
+        x = rng.standard_normal((n, d)).astype(np.float32)
+        x[:, rng.choice(d, 4, replace=False)] *= 20.0  # outlier channels
+        x = _bf16(x)
+        s = rng.choice([-1.0, 1.0], d)
+        h = fp8.hadamard(d)
+        xs = x.astype(np.float64) * s
+        exact = xs @ h
+        # the float64 product is exact: compare with integers
+        _, e = np.frexp(xs[xs != 0])
+        k = int(8 - e.min())  # 2^k x is an integer for every element
+        xi = np.rint(np.ldexp(xs, k)).astype(np.int64)
+        assert np.array_equal(np.ldexp(xi.astype(np.float64), -k), xs)
+        yi = xi @ h.astype(np.int64)
+        assert np.abs(yi).max() < 2 ** 53
+        assert np.array_equal(np.ldexp(yi.astype(np.float64), -k), exact)
+        # the float32 butterflies stay within their error bound
+        y32 = fp8.rotate(x, s).astype(np.float64)
+        bound = 1.01 * math.log2(d) * u * np.abs(x).astype(np.float64).sum(
+            axis=1, keepdims=True)
+        err = np.abs(y32 - exact)
+        assert np.all(err <= bound), float((err / bound).max())
+        assert err.max() > 0  # the inputs do exercise the rounding
+        # code decisions, 64-row blocks, the float32 path's multiplier
+        for b0 in range(0, n, 64):
+            blk32 = y32[b0:b0 + 64].astype(np.float32)
+            _, mul = fp8._block_scale(np.abs(blk32).max())
+            c32 = fp8.e4m3_encode(np.float32(blk32 * mul))
+            z = exact[b0:b0 + 64] * np.float64(mul)
+            c64 = fp8.e4m3_encode(z)
+            diff = c32 != c64
+            codes_total += diff.size
+            if not diff.any():
+                continue
+            a = np.abs(z[diff])
+            j = np.clip(np.searchsorted(mids, a), 1, len(mids) - 1)
+            dist = np.minimum(np.abs(a - mids[j - 1]), np.abs(a - mids[j]))
+            tol = (bound[b0:b0 + 64] * np.ones_like(z))[diff] * float(mul) \
+                + 2.0 * u * a
+            assert np.all(dist <= tol), float((dist / tol).max())
+            changed_total += int(diff.sum())
+    assert changed_total <= 5e-4 * codes_total, (changed_total, codes_total)
+
+
 FP8_CHECKS = [
     check_e4m3_format,
     check_e4m3_encode,
     check_hadamard_algebra,
+    check_fwht_f32_against_exact_rotation,
     check_quantize_blocks,
     check_rotation_preserves_attention,
     check_attention_quantized,

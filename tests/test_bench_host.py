@@ -80,3 +80,30 @@ def test_allowed_pairs_matches_mask_count():
                              window_right=w.window_right, sinks=w.sinks)
             total += int(m.sum())
         assert bench.allowed_pairs(w, sl) == total
+
+
+def test_prefill_roofline_takes_the_longer_bound():
+    """gpt2-small-causal-padded moves more bytes per FLOP than the ridge
+    (2.5 PFLOP/s over 8 TB/s, 312 FLOP/B) allows: its bound is HBM.  The
+    headline grouped-query prefill is MFMA-bound."""
+    w = synth.by_name("gpt2-small-causal-padded")
+    sl = synth.make_inputs(w, 2)["seqlens"]
+    r = bench.prefill_roofline(w, sl, 1e-4)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["algorithmic_flop_per_launch"] / \
+        r["algorithmic_bytes_per_launch"] < 312.5
+    live = int(np.minimum(sl, 1024).sum())
+    assert r["algorithmic_bytes_per_launch"] == \
+        live * 12 * (2 * 64 * 2 + 4) + live * 12 * 2 * 64 * 2
+    assert abs(r["achieved"] - r["algorithmic_bytes_per_launch"] / 1e-4 /
+               1e9) < 0.1
+    wp = synth.by_name("gqa-causal-prefill")
+    rp = bench.prefill_roofline(wp, None, 1e-3)
+    assert rp["bound"] == "mfma" and rp["unit"] == "TFLOP/s"
+    assert rp["algorithmic_flop_per_launch"] == 4 * 128 * 28 * 4 * \
+        (4096 * 4097 // 2)
+
+
+def test_cpu_model_reads_proc_cpuinfo():
+    m = bench.cpu_model()
+    assert m is None or isinstance(m, str) and m

@@ -150,3 +150,79 @@ def test_torch_wrapper_rejects_cpu_tensors():
         mi.attn(q, q, q)
     with pytest.raises(TypeError):
         mi.attn(q, q, q.float())
+
+
+def call_quant(a):
+    return mi.attn_fp8_quantize(
+        a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+        a["d"], a["seqlens"], a.get("signs", 0), a.get("per_tensor", 0),
+        a.get("q8", P), a.get("sq", P), a.get("k8", P), a.get("sk", P),
+        a.get("v8t", P), a.get("sv", P), a["stream"])
+
+
+# the quantizer takes the shape checks of the forward (no scale or mask
+# arguments), non-null outputs, 16-byte aligned codes and 4-byte aligned
+# scales, and the one-resource limit on a sequence's bytes
+BAD_QUANT = [b for b in BAD if b[2] not in ("causal", "finite")
+             and "lse" not in b[0] and "o" not in b[0]
+             and "window" not in b[0]] + [
+    (dict(q8=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(sk=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(v8t=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(k8=P + 8), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(sq=P + 2), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(B=1, Hq=1, Hkv=1, Nq=64, Nk=1 << 23, d=128),
+     mi.MIATTN_ERR_UNSUPPORTED, "2^31"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", BAD_QUANT,
+                         ids=[str(b[0]) for b in BAD_QUANT])
+def test_fp8_quantize_rejected_on_host(over, code, msg):
+    rc = call_quant(good(**over))
+    assert rc == code
+    err = mi.attn_last_error()
+    assert "attn_fp8_quantize" in err and msg in err, err
+
+
+def call_fwd8(a):
+    return mi.attn_fwd_fp8(
+        a.get("q8", P), a.get("sq", P), a.get("k8", P), a.get("sk", P),
+        a.get("v8t", P), a.get("sv", P), a["o"], a["lse"], a["B"], a["Hq"],
+        a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a.get("rotated", 0),
+        a["causal"], a["window"], a.get("window_right", 0),
+        a.get("sinks", 0), a["seqlens"], a["stream"])
+
+
+# the FP8 forward takes the masked entry points' checks (its code buffers
+# stand where q, k, v stand there), non-null 4-byte aligned scales and the
+# one-resource limit
+BAD_FWD8 = [b for b in BAD_MASKED
+            if not any(key in b[0] for key in ("q", "v"))] + [
+    (dict(q8=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(v8t=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(k8=P + 4), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(sq=0), mi.MIATTN_ERR_INVALID, "non-null"),
+    (dict(sv=P + 1), mi.MIATTN_ERR_INVALID, "aligned"),
+    (dict(B=1, Hq=1, Hkv=1, Nq=64, Nk=1 << 23, d=128),
+     mi.MIATTN_ERR_UNSUPPORTED, "2^31"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", BAD_FWD8,
+                         ids=[str(b[0]) for b in BAD_FWD8])
+def test_fwd_fp8_rejected_on_host(over, code, msg):
+    rc = call_fwd8(good(**over))
+    assert rc == code
+    err = mi.attn_last_error()
+    assert "attn_fwd_fp8" in err and msg in err, err
+
+
+@pytest.mark.parametrize("Nq,Nk,d", [(1 << 23, 1 << 23, 128),
+                                     (64, (1 << 24) - 63, 64)])
+def test_backward_rejects_sequences_past_one_resource(Nq, Nk, d):
+    """The backward kernels address a whole sequence through one buffer
+    resource (32-bit byte range): 2^31 bytes or more is refused."""
+    rc = call_bwd(good(B=1, Hq=1, Hkv=1, Nq=Nq, Nk=Nk, d=d))
+    assert rc == mi.MIATTN_ERR_UNSUPPORTED
+    assert "2^31" in mi.attn_last_error()

@@ -1,8 +1,10 @@
 """GPU parity: libmiattn (through its C ABI) against the fp64 oracle.
 
-Reduced sizes compare every row and span several 128-row query blocks and
-64-key tiles with ragged tails; the five workloads run at full size with
-sampled rows (config 2 and the fp32 case compare every row).  Edge cases:
+Reduced sizes compare every row and span several query blocks and 64-key
+tiles with ragged tails.  The five workloads run at full size with three
+seeds each: every row of the fp32 case, the padded GPT-2-shaped prefill, the
+grouped-query prefill and the decode step; four whole (batch, head) slices
+and sampled rows of the others for the 16384-token sliding window.  Edge cases:
 empty sequences, one valid key, window of one, N below one tile, GQA groups
 of 1, 2, 4, 7 and 16, negative and zero scale, NaN in the padding.
 """
@@ -131,9 +133,29 @@ def test_config_fp32_single_head():
         gu.check_full(w.name, w, seed)
 
 
-def test_config_gpt2_small_causal_padded_all_rows():
-    w = synth.by_name("gpt2-small-causal-padded")
-    gu.check_full(w.name, w, 2)
+# every row of the full-size workloads the oracle finishes in seconds, three
+# seeds each (k, 100 + k, 200 + k for workload k; the first is the bench's)
+@pytest.mark.parametrize("name,seed", [
+    (name, base + off)
+    for name, base in (("gpt2-small-causal-padded", 2),
+                       ("gqa-causal-prefill", 3), ("decode-gqa", 5))
+    for off in (0, 100, 200)])
+def test_config_full_size_all_rows(name, seed):
+    w = synth.by_name(name)
+    gu.check_full(name, w, seed)
+
+
+@pytest.mark.parametrize("seed,slices", [
+    (4, [(0, 0), (0, 15), (1, 7), (1, 15)]),
+    (104, [(0, 3), (1, 12)]),
+    (204, [(1, 0), (0, 9)])])
+def test_sliding_window_causal_whole_slices(seed, slices):
+    """sliding-window-causal at full size (B=2 H=16 N=16384 d=64, window
+    1024): whole (batch, head) slices, every query row, against the oracle's
+    dense masked rows (16384 keys each); sampled rows of the other slices
+    are checked by test_config_full_size_sampled."""
+    w = synth.by_name("sliding-window-causal")
+    gu.check_whole_slices(w.name, w, seed, slices)
 
 
 # ---- Nq new rows against a longer key sequence (1 < Nq < Nk) ---------------
@@ -254,12 +276,9 @@ def test_masks_full_size_sampled(name, seed):
 
 
 @pytest.mark.parametrize("name,seed", [
-    ("gpt2-small-causal-padded", 102),
-    ("gqa-causal-prefill", 3),
-    ("gqa-causal-prefill", 103),
     ("sliding-window-causal", 4),
-    ("decode-gqa", 5),
-    ("decode-gqa", 105),
+    ("sliding-window-causal", 104),
+    ("sliding-window-causal", 204),
 ])
 def test_config_full_size_sampled(name, seed):
     w = synth.by_name(name)

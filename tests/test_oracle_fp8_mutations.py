@@ -96,7 +96,35 @@ def _quantize_all_v_rotated(q, k, v, seqlens, *, signs=None,
     return out
 
 
+def _fwht_with(round_stage=None, swap=False):
+    def fwht(x):
+        y = np.array(x, dtype=np.float32, copy=True)
+        d = y.shape[-1]
+        h = 1
+        while h < d:
+            y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+            a = y[..., 0, :].copy()
+            b = y[..., 1, :].copy()
+            y[..., 0, :] = a + b
+            y[..., 1, :] = (b - a) if swap else (a - b)  # planted: sign
+            if round_stage:
+                y = round_stage(y)  # planted: a stage kept in low precision
+            y = y.reshape(y.shape[:-3] + (d,))
+            h *= 2
+        return y
+    return dict(fwht_f32=fwht,
+                rotate=lambda x, s: fwht(np.asarray(x, np.float32) *
+                                         np.asarray(s, np.float32)))
+
+
+def _to_bf16(y):
+    from tests.oracle_fp8_checks import _bf16
+    return _bf16(y).reshape(y.shape)
+
+
 MUTANTS = {
+    "fwht_in_bf16": _fwht_with(round_stage=_to_bf16),
+    "fwht_butterfly_sign": _fwht_with(swap=True),
     "v_rotated_too": dict(quantize_all=_quantize_all_v_rotated),
     "encode_truncates": dict(e4m3_encode=_encode_trunc),
     "encode_ties_away": dict(e4m3_encode=_encode_ties_away),

@@ -7,10 +7,11 @@ is not built, importing the binding's entry points raises.
 
 Entry points with the C names (raw pointers as Python ints):
     attn_fwd, attn_fwd_f32, attn_fwd_masked, attn_fwd_masked_f32,
+    attn_bwd, attn_fp8_quantize, attn_fwd_fp8,
     attn_last_error, attn_release
-Convenience wrapper on torch tensors:
+Convenience wrappers on torch tensors:
     attn(q, k, v, causal=False, window=0, seqlens=None, scale=None,
-         window_right=0, sinks=0)
+         window_right=0, sinks=0), attn_backward, fp8_quantize, attn_fp8
 """
 
 import ctypes
@@ -27,8 +28,9 @@ MIATTN_ERR_HIP = -3
 MIATTN_ERR_NOMEM = -4
 
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_masked",
-           "attn_fwd_masked_f32", "attn_bwd", "attn_fp8_quantize",
-           "attn_fwd_fp8", "attn_last_error", "attn_release")
+           "attn_fwd_masked_f32", "attn_bwd",
+           "attn_fp8_quantize", "attn_fwd_fp8", "attn_last_error",
+           "attn_release")
 
 _lib = None
 
@@ -141,41 +143,137 @@ def attn_release():
     load().attn_release()
 
 
+def _need(t, name, dtype, shape, device):
+    """Raises ValueError unless tensor `t` has this dtype and shape, is
+    contiguous and lives on `device`: the kernels read or write exactly that
+    many elements at that address."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got "
+                         f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _seqlens_ptr(seqlens, B, device):
+    """Device address of an int32 [B] valid-length tensor (0 for None)."""
+    import torch
+    if seqlens is None:
+        return 0
+    _need(seqlens, "seqlens", torch.int32, (B,), device)
+    return seqlens.data_ptr()
+
+
+def _check_qkv(q, k, v, dtypes, require_gpu=True):
+    """(B, Hq, Hkv, Nq, Nk, d) of q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d], after
+    checking that they share one dtype out of `dtypes`, are contiguous 4-d
+    tensors on one device (a GPU unless require_gpu is False) and agree in
+    B and d."""
+    if q.dtype not in dtypes:
+        raise TypeError(f"q must be one of {dtypes}, got {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    if require_gpu and not q.is_cuda:
+        raise ValueError("q, k, v must be GPU tensors")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or \
+            k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k "
+                         f"{tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def check_attn_args(q, k, v, out=None, lse=None, seqlens=None,
+                    require_gpu=True):
+    """The checks `attn` makes before any launch: q, k, v as in _check_qkv
+    (bfloat16 or float32), `out` like q, `lse` float32 [B, Hq, Nq] and
+    `seqlens` int32 [B], all contiguous on q's device (None: not given).
+    Returns (B, Hq, Hkv, Nq, Nk, d)."""
+    import torch
+    shp = _check_qkv(q, k, v, (torch.bfloat16, torch.float32), require_gpu)
+    B, Hq, Hkv, Nq, Nk, d = shp
+    if out is not None:
+        _need(out, "out", q.dtype, q.shape, q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, Nq), q.device)
+    _seqlens_ptr(seqlens, B, q.device)
+    return shp
+
+
+def check_backward_args(q, k, v, o, lse, dout, seqlens=None,
+                        require_gpu=True):
+    """The checks `attn_backward` makes before any launch: q, k, v, o, dout
+    bfloat16 (o and dout like q), lse float32 [B, Hq, Nq], seqlens int32
+    [B], all contiguous on q's device."""
+    import torch
+    shp = _check_qkv(q, k, v, (torch.bfloat16,), require_gpu)
+    B, Hq, Hkv, Nq, Nk, d = shp
+    _need(o, "o", torch.bfloat16, q.shape, q.device)
+    _need(dout, "dout", torch.bfloat16, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (B, Hq, Nq), q.device)
+    _seqlens_ptr(seqlens, B, q.device)
+    return shp
+
+
+def fp8_buffer_shapes(B, Hq, Hkv, Nq, Nk, d):
+    """Shapes of the quantized buffers (see attn_fp8_quantize); Nk is padded
+    to whole 64-key tiles."""
+    nkp = (Nk + 63) // 64 * 64
+    return dict(q8=(B, Hq, Nq, d), sq=(B, Hq, (Nq + 63) // 64),
+                k8=(B, Hkv, nkp, d), sk=(B, Hkv, nkp // 64),
+                v8t=(B, Hkv, nkp // 64, d, 64), sv=(B, Hkv, nkp // 64))
+
+
+def check_fp8_state(z, out=None, lse=None, seqlens=None):
+    """The checks `attn_fp8` makes before any launch: every buffer of `z`
+    (what fp8_quantize returned) has the shape its recorded problem needs
+    and its dtype (codes uint8, scales float32), all on one device; out is
+    bfloat16 [B, Hq, Nq, d], lse float32 [B, Hq, Nq], seqlens int32 [B].
+    Returns (B, Hq, Hkv, Nq, Nk, d)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = z["shape"]
+    dev = z["q8"].device
+    for name, shp in fp8_buffer_shapes(B, Hq, Hkv, Nq, Nk, d).items():
+        dt = torch.float32 if name.startswith("s") else torch.uint8
+        _need(z[name], name, dt, shp, dev)
+    if out is not None:
+        _need(out, "out", torch.bfloat16, (B, Hq, Nq, d), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, Nq), dev)
+    _seqlens_ptr(seqlens, B, dev)
+    return B, Hq, Hkv, Nq, Nk, d
+
+
 def attn(q, k, v, *, causal=False, window=0, seqlens=None, scale=None,
          out=None, lse=None, stream=None, window_right=0, sinks=0):
     """Attention on torch device tensors.
 
     q: [B, Hq, Nq, d], k/v: [B, Hkv, Nk, d], all bfloat16 or all float32,
     contiguous, on the same GPU.  seqlens: int32 device tensor [B] or None.
-    Returns (o, lse) with o like q and lse float32 [B, Hq, Nq].  The default
-    scale is 1/sqrt(d).  window_right or sinks > 0, or a window without the
-    causal mask, select the masked entry points (window is then the left
-    limit of the neighbourhood).
+    out (like q) and lse (float32 [B, Hq, Nq]) may be given; they are
+    checked like the inputs.  Returns (o, lse).  The default scale is
+    1/sqrt(d).  window_right or sinks > 0, or a window without the causal
+    mask, select the masked entry points (window is then the left limit of
+    the neighbourhood).
     """
     import torch
-    if q.dtype != k.dtype or q.dtype != v.dtype:
-        raise TypeError("q, k, v must share one dtype")
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q, k, v must be bfloat16 or float32")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("q, k, v must be contiguous 4-d GPU tensors")
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nk, _ = k.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("shape mismatch between q, k, v")
+    B, Hq, Hkv, Nq, Nk, d = check_attn_args(q, k, v, out, lse, seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    sl = 0
-    if seqlens is not None:
-        if seqlens.dtype != torch.int32 or not seqlens.is_cuda or \
-                seqlens.numel() != B:
-            raise ValueError("seqlens must be an int32 GPU tensor of size B")
-        sl = seqlens.data_ptr()
+    sl = _seqlens_ptr(seqlens, B, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     bf = q.dtype == torch.bfloat16
@@ -204,28 +302,11 @@ def attn_backward(q, k, v, o, lse, dout, *, causal=False, window=0,
     o.  Returns new tensors dq like q, dk and dv like k.
     """
     import torch
-    for t in (q, k, v, o, dout):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or \
-                not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("q, k, v, o, dout must be contiguous 4-d "
-                             "bfloat16 GPU tensors")
-    if lse.dtype != torch.float32 or not lse.is_cuda or \
-            not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 GPU tensor")
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nk, _ = k.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or \
-            o.shape != q.shape or dout.shape != q.shape or \
-            tuple(lse.shape) != (B, Hq, Nq):
-        raise ValueError("shape mismatch between q, k, v, o, lse, dout")
+    B, Hq, Hkv, Nq, Nk, d = check_backward_args(q, k, v, o, lse, dout,
+                                                seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    sl = 0
-    if seqlens is not None:
-        if seqlens.dtype != torch.int32 or not seqlens.is_cuda or \
-                seqlens.numel() != B:
-            raise ValueError("seqlens must be an int32 GPU tensor of size B")
-        sl = seqlens.data_ptr()
+    sl = _seqlens_ptr(seqlens, B, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     dq = torch.empty_like(q)
@@ -246,34 +327,20 @@ def fp8_quantize(q, k, v, *, seqlens=None, signs=None, per_tensor=False,
     """E4M3 codes and block scales of bfloat16 GPU tensors q, k, v (see
     attn_fp8_quantize in include/miattn.h).  signs: int8 GPU tensor of d
     entries +-1 (rotate Q and K) or None.  Returns a dict with q8, sq, k8,
-    sk, v8t, sv, and `rotated`."""
+    sk, v8t, sv, `rotated` and the problem's `shape`."""
     import torch
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or \
-                not t.is_contiguous() or t.dim() != 4:
-            raise ValueError("q, k, v must be contiguous 4-d bfloat16 GPU "
-                             "tensors")
-    B, Hq, Nq, d = q.shape
-    _, Hkv, Nk, _ = k.shape
-    nkp = (Nk + 63) // 64 * 64
+    B, Hq, Hkv, Nq, Nk, d = _check_qkv(q, k, v, (torch.bfloat16,))
     dev = q.device
-    out = dict(
-        q8=torch.empty((B, Hq, Nq, d), dtype=torch.uint8, device=dev),
-        sq=torch.empty((B, Hq, (Nq + 63) // 64), dtype=torch.float32,
-                       device=dev),
-        k8=torch.empty((B, Hkv, nkp, d), dtype=torch.uint8, device=dev),
-        sk=torch.empty((B, Hkv, nkp // 64), dtype=torch.float32, device=dev),
-        v8t=torch.empty((B, Hkv, nkp // 64, d, 64), dtype=torch.uint8,
-                        device=dev),
-        sv=torch.empty((B, Hkv, nkp // 64), dtype=torch.float32, device=dev),
-        rotated=signs is not None)
     sgn = 0
     if signs is not None:
-        if signs.dtype != torch.int8 or not signs.is_cuda or \
-                signs.numel() != d:
-            raise ValueError("signs must be an int8 GPU tensor of d entries")
+        _need(signs, "signs", torch.int8, (d,), dev)
         sgn = signs.data_ptr()
-    sl = 0 if seqlens is None else seqlens.data_ptr()
+    sl = _seqlens_ptr(seqlens, B, dev)
+    out = {name: torch.empty(shp, dtype=torch.float32 if name[0] == "s"
+                             else torch.uint8, device=dev)
+           for name, shp in fp8_buffer_shapes(B, Hq, Hkv, Nq, Nk,
+                                              d).items()}
+    out["rotated"] = signs is not None
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     rc = attn_fp8_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, Hq,
@@ -290,9 +357,10 @@ def fp8_quantize(q, k, v, *, seqlens=None, signs=None, per_tensor=False,
 
 def attn_fp8(z, *, causal=False, window=0, seqlens=None, scale=None,
              window_right=0, sinks=0, out=None, lse=None, stream=None):
-    """Attention on the output of fp8_quantize; returns (o bf16, lse)."""
+    """Attention on the output of fp8_quantize; returns (o bf16, lse).
+    seqlens must be the valid lengths the codes were quantized with."""
     import torch
-    B, Hq, Hkv, Nq, Nk, d = z["shape"]
+    B, Hq, Hkv, Nq, Nk, d = check_fp8_state(z, out, lse, seqlens)
     dev = z["q8"].device
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -300,7 +368,7 @@ def attn_fp8(z, *, causal=False, window=0, seqlens=None, scale=None,
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
-    sl = 0 if seqlens is None else seqlens.data_ptr()
+    sl = _seqlens_ptr(seqlens, B, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     rc = attn_fwd_fp8(z["q8"].data_ptr(), z["sq"].data_ptr(),

@@ -73,19 +73,30 @@ int validate(const char* fn, const void* q, const void* k, const void* v,
 }
 
 // ---- workspace of the decode and backward passes, one per device ---------
+// The lock is held from the size check through the launch that uses the
+// buffer, so a growth by another host thread (which frees the old buffer)
+// cannot slip in between.  Growth calls hipFree and hipMalloc: the free
+// waits for the device to finish the work still using the old buffer.
 constexpr int kMaxDevices = 64;
 std::mutex g_ws_mu;
 void* g_ws[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
 
-int workspace(size_t need, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+int current_device(int* dev) {
+  const hipError_t e = hipGetDevice(dev);
   if (e != hipSuccess)
     return fail(MIATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= kMaxDevices)
-    return fail(MIATTN_ERR_HIP, "device index %d out of range", dev);
-  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (*dev < 0 || *dev >= kMaxDevices)
+    return fail(MIATTN_ERR_HIP, "device index %d out of range", *dev);
+  return MIATTN_OK;
+}
+
+// Caller holds g_ws_mu.
+int workspace_locked(size_t need, void** out) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != MIATTN_OK) return rc;
+  hipError_t e;
   if (g_ws_bytes[dev] < need) {
     if (g_ws[dev]) {
       e = hipFree(g_ws[dev]);  // waits for work still using it
@@ -104,6 +115,19 @@ int workspace(size_t need, void** out) {
     g_ws_bytes[dev] = need;
   }
   *out = g_ws[dev];
+  return MIATTN_OK;
+}
+
+// Sequences whose whole extent is addressed by one 32-bit buffer resource
+// (the backward and FP8 kernels): q/o rows of a (batch, head) and k/v rows,
+// padded to whole 64-key tiles, must span less than 2^31 bytes.
+int check_sequence_bytes(const char* fn, int Nq, int Nk, int d) {
+  const long long lim = 1LL << 31;
+  const long long nkp = ((long long)Nk + 63) / 64 * 64;
+  if ((long long)Nq * d * 2 >= lim || nkp * d * 2 >= lim)
+    return fail(MIATTN_ERR_UNSUPPORTED,
+                "%s: one sequence of Nq=%d or Nk=%d rows at d=%d spans 2^31 "
+                "bytes or more", fn, Nq, Nk, d);
   return MIATTN_OK;
 }
 
@@ -138,8 +162,9 @@ int run_bf16(const char* fn, const void* q, const void* k, const void* v,
   hipError_t e;
   int rc;
   if (miattn::decode_takes(p)) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
     void* ws = nullptr;
-    rc = workspace(miattn::decode_workspace_bytes(p), &ws);
+    rc = workspace_locked(miattn::decode_workspace_bytes(p), &ws);
     if (rc != MIATTN_OK) return rc;
     e = miattn::launch_decode_bf16(q, k, v, o, lse, p, ws, st);
   } else {
@@ -233,11 +258,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(MIATTN_ERR_INVALID,
                 "%s: dout, dq, dk and dv must be 16-byte aligned", fn);
+  rc = check_sequence_bytes(fn, Nq, Nk, d);
+  if (rc != MIATTN_OK) return rc;
   const miattn::Problem p =
       make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
                    window_right, sinks, seqlens);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
   void* ws = nullptr;
-  rc = workspace(miattn::bwd_workspace_bytes(p), &ws);
+  rc = workspace_locked(miattn::bwd_workspace_bytes(p), &ws);
   if (rc != MIATTN_OK) return rc;
   const hipError_t e =
       miattn::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, p, ws,
@@ -266,6 +294,8 @@ int attn_fp8_quantize(const void* q, const void* k, const void* v, int B,
     return fail(MIATTN_ERR_INVALID,
                 "%s: q8, k8, v8t must be 16-byte aligned, the scales 4-byte",
                 fn);
+  rc = check_sequence_bytes(fn, Nq, Nk, d);
+  if (rc != MIATTN_OK) return rc;
   const miattn::Problem p =
       make_problem(B, Hq, Hkv, Nq, Nk, d, 1.0f, 0, 0, 0, 0, seqlens);
   const hipError_t e = miattn::launch_fp8_quantize(
@@ -292,6 +322,8 @@ int attn_fwd_fp8(const void* q8, const float* sq, const void* k8,
        reinterpret_cast<uintptr_t>(sv)) & 3u)
     return fail(MIATTN_ERR_INVALID, "%s: the scales must be 4-byte aligned",
                 fn);
+  rc = check_sequence_bytes(fn, Nq, Nk, d);
+  if (rc != MIATTN_OK) return rc;
   const miattn::Problem p =
       make_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
                    window_right, sinks, seqlens);
