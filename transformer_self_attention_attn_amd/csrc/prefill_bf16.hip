@@ -187,7 +187,8 @@ template <int I>
 using ic = std::integral_constant<int, I>;
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
+    PrefillParams p) {
   using C = Cfg<D, NW>;
   // one LDS object per ring slot: the compiler keeps per-object alias
   // scopes, which lets reads of one slot proceed while another is filled
@@ -208,19 +209,35 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   };
 
   // ---- block -> (batch, head, query block) --------------------------------
+  // Blocks are dealt round-robin to the 8 XCDs (block id mod 8).  Each XCD
+  // gets whole (batch, K/V head) groups, so a group's K/V tiles meet in one
+  // L2.  Under the causal mask a query block's work grows with its index:
+  // when the groups divide evenly over the XCDs, each XCD runs its blocks
+  // heaviest first across all of its groups (longest job first), so that no
+  // long diagonal block starts late; otherwise heaviest first within each
+  // group.
   const int n = p.total;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int slot = bid / kXcds;
-  const int per = n / kXcds;
-  const int rem = n % kXcds;
-  const int lid = xcd * per + min(xcd, rem) + slot;
-
-  const int per_grp = p.G * p.nqb;
-  const int grp = lid / per_grp;
-  const int r0 = lid - grp * per_grp;
-  const int qrank = r0 / p.G;
-  const int hh = r0 - qrank * p.G;
+  const int ngrp = p.B * p.Hkv;
+  int grp, qrank, hh;
+  if (p.causal && ngrp % kXcds == 0) {
+    const int gpx = ngrp / kXcds;  // groups per XCD
+    qrank = slot / (gpx * p.G);
+    const int r1 = slot - qrank * gpx * p.G;
+    grp = xcd * gpx + r1 / p.G;
+    hh = r1 - (r1 / p.G) * p.G;
+  } else {
+    const int per = n / kXcds;
+    const int rem = n % kXcds;
+    const int lid = xcd * per + min(xcd, rem) + slot;
+    const int per_grp = p.G * p.nqb;
+    grp = lid / per_grp;
+    const int r0 = lid - grp * per_grp;
+    qrank = r0 / p.G;
+    hh = r0 - qrank * p.G;
+  }
   const int qb = p.causal ? (p.nqb - 1 - qrank) : qrank;
   const int b = grp / p.Hkv;
   const int hk = grp - b * p.Hkv;
@@ -364,14 +381,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
                           rows * D * 2);
   };
   // Interleaved loads (issued during X): every wave issues KLW + VLW of
-  // them per tile.  A wave without a load number m (uneven split), and a step
-  // with no tile to load, writes into a 1 KB sink instead of the slot.
+  // them per tile.  A wave without a load number m (uneven split) writes
+  // into a 1 KB sink instead of the slot; a step with no tile to load reads
+  // through an empty resource, whose zeros land in a slot nothing reads
+  // before it is loaded again.
   __shared__ __attribute__((aligned(16))) uint16_t Sink[512];
-  auto dma_il = [&](miattn_i32x4 rs, uint16_t* slot, bool real, unsigned vo,
-                    int i, int nloads) {
-    const bool ok = real && i < nloads;
-    miattn_buffer_load_lds(rs, (lds_void*)(ok ? slot + i * 512 : Sink), 16,
-                           (int)vo, 0, 0, 0);
+  auto dma_il = [&](miattn_i32x4 rs, uint16_t* slot, unsigned vo, int i,
+                    int nloads) {
+    miattn_buffer_load_lds(rs, (lds_void*)(i < nloads ? slot + i * 512 : Sink),
+                           16, (int)vo, 0, 0, 0);
   };
 
   auto dma_k = [&](auto slot_c, int t) {
@@ -433,7 +451,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // with this tile's exponentials (at the end of the range it reads a stale
   // slot and the result is dropped).
   // kbi / vbi: tile bases of this step's interleaved K / V loads (into slots
-  // SLK / SLV); real_k / real_v: whether they are this step's real loads.
+  // SLK / SLV).
   // X(t): mask and maximum of tile t's scores `sc`, lazy rescale, and the
   // S^T product of tile t+1 (K slot SK) into `sn`, interleaved with tile t's
   // exponentials and with this wave's share of a tile load pair (K into slot
@@ -441,20 +459,41 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   // stay in
   // `sc` (fp32) for Y(t).
   auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, miattn_i32x4 krs,
-                   miattn_i32x4 vrs, bool real_k, bool real_v, int t,
+                   miattn_i32x4 vrs, int t,
                    f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int SK = decltype(sk_c)::value;
     const int j0 = t * kKT;
     float mx = mx_pre;
     // lane holds keys j0 + mb*32 + g*16 + r (r = 0..15) of query qi
     if (!tile_full(t)) {
+      // this lane's keys of block mb are jb + r, r = 0 .. 15; the bounds are
+      // taken relative to jb so that each test compares with a constant r
+      if (p.window == 0 && p.sinks == 0) {  // keys below hw only
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
+          const int hi = hw - (j0 + mb * 32 + g * 16);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + mb * 32 + g * 16 + r;
-          if ((j < lo || j >= hw) && j >= sk) sc[mb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (r >= hi) sc[mb][r] = -INFINITY;
         }
+      } else if (p.sinks == 0) {  // keys in [lo, hw)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int jb = j0 + mb * 32 + g * 16;
+          const int lor = lo - jb, hi = hw - jb;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r < lor || r >= hi) sc[mb][r] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + mb * 32 + g * 16 + r;
+            if ((j < lo || j >= hw) && j >= sk) sc[mb][r] = -INFINITY;
+          }
+      }
       mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -513,10 +552,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       }
       // this step's loads, one per MFMA slot
       if (i < C::KLW)
-        dma_il(krs, kslot(slk_c), real_k, kvo[i], wave + NW * i, C::KLOADS);
+        dma_il(krs, kslot(slk_c), kvo[i], wave + NW * i, C::KLOADS);
       else if (i < C::KLW + C::VLW)
-        dma_il(vrs, vslot(slv_c), real_v, vvo[i - C::KLW],
-               wave + NW * (i - C::KLW), C::VLOADS);
+        dma_il(vrs, vslot(slv_c), vvo[i - C::KLW], wave + NW * (i - C::KLW),
+               C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);  // VALU
@@ -627,7 +666,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     if (!il && ld_k) dma_k(ic<SLK>(), rk);
     if (il) {
       tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), tile_rsrc(kg, rk, ld_k),
-            tile_rsrc(vg, rv, ld_v), ld_k, ld_v, rt, sc, sn);
+            tile_rsrc(vg, rv, ld_v), rt, sc, sn);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
