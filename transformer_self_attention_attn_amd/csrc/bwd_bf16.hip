@@ -109,10 +109,7 @@ struct BCfg {
 // 256-byte bank line; d=64: two).
 template <int D>
 __device__ inline int swz(int r) {
-  if constexpr (D == 128)
-    return 4 * (r & 3) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
-  else
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+  return lanes::bwd_swz(D, r);
 }
 
 // One wave-wide direct-to-LDS load of a [64][D] tile: wave load i fills
@@ -125,11 +122,8 @@ __device__ inline int swz(int r) {
 // wave load i: row s / CH, logical chunk (s % CH) ^ swz(row).
 template <int D>
 __device__ inline unsigned tile_src_off(int i, int lane) {
-  using C = BCfg<D>;
-  const int s = i * 64 + lane;
-  const int r = s / C::CH;
-  const int c = (s % C::CH) ^ swz<D>(r);
-  return (unsigned)((r * D + c * 8) * 2);
+  static_assert(BCfg<D>::LOADS == lanes::bwd_tile_loads(D), "tile loads");
+  return lanes::bwd_tile_src(D, i, lane);
 }
 
 // Element offset of this lane's row-wise A-operand piece: tile row
@@ -851,11 +845,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 }
 
 constexpr int kDkdvNW = 4;   // 128 keys per workgroup
+static_assert(kDkdvNW == lanes::kBwdWaves, "shared lane layout");
 // dQ: 128 rows per workgroup and two workgroups per CU (two waves per SIMD
 // from independent workgroups, which drift out of phase; one 8-wave
 // workgroup per CU was 5-10% slower at d=128)
 constexpr int kDqNW128 = 4;
 constexpr int kDqNW64 = 4;
+static_assert(kDqNW128 == lanes::kBwdWaves && kDqNW64 == lanes::kBwdWaves,
+              "shared lane layout");
 
 template <int D, int NWK, int NWQ>
 hipError_t launch_all(BwdParams p, hipStream_t st) {

@@ -9,6 +9,8 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "lane_layout.h"
+
 typedef int miattn_i32x4 __attribute__((ext_vector_type(4)));
 
 // The direct-to-LDS buffer load (buffer_load_dword* ... lds), declared by
@@ -93,9 +95,7 @@ __device__ inline void rows_of_key(const Seq& s, int causal, int wl, int wr,
 // Row of a 32-row MFMA A-operand block that holds tile row m: with this order
 // the 32x32 accumulator gives lane group g (lanes 32g .. 32g+31) the 16
 // consecutive tile rows g*16 .. g*16+15 of each 32-row block.
-__device__ inline int mfma_row(int m) {
-  return (m >> 5) * 32 + ((m >> 2) & 1) * 16 + ((m & 31) >> 3) * 4 + (m & 3);
-}
+__device__ inline int mfma_row(int m) { return lanes::mfma_row(m); }
 
 // Buffer resource over `bytes` bytes at `base` (stride 0, 32-bit data
 // format): a load at or past the end reads zeros.

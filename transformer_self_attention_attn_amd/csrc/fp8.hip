@@ -88,12 +88,9 @@ constexpr float kPScale = 256.0f;
 // V^T tile rows are 64 bytes read 16 consecutive rows at a time.
 template <int D>
 __device__ inline int swz_k(int r) {
-  if constexpr (D == 128)
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
-  else
-    return ((r >> 2) & 1) + 2 * ((r >> 4) & 1);
+  return lanes::fp8_swz_k(D, r);
 }
-__device__ inline int swz_v(int r) { return (r >> 2) & 3; }
+__device__ inline int swz_v(int r) { return lanes::fp8_swz_v(r); }
 
 // ---------------------------------------------------------------------------
 // quantizer
@@ -415,17 +412,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int m = 0; m < LW; ++m) {
     const int u2 = wave + NW * m;
-    const int i = u2 < KT / 1024 ? u2 : u2 - KT / 1024;
-    const int sl = i * 64 + lane;
-    if (u2 < KT / 1024) {
-      const int row = sl / (D / 16);
-      const int c = (sl % (D / 16)) ^ swz_k<D>(row);
-      toffs[m] = (unsigned)(row * D + 16 * c);
-    } else {
-      const int row = sl / 4;
-      const int c = (sl % 4) ^ swz_v(row);
-      toffs[m] = (unsigned)(row * 64 + 16 * c);
-    }
+    static_assert(KT / 1024 == lanes::fp8_k_loads(D) &&
+                      KT / 1024 == lanes::fp8_v_loads(D),
+                  "tile loads");
+    toffs[m] = u2 < KT / 1024 ? lanes::fp8_k_src(D, u2, lane)
+                              : lanes::fp8_v_src(u2 - KT / 1024, lane);
   }
   const size_t kvh = (size_t)(b * p.Hkv + hk) * p.Nkp * D;
   const miattn_i32x4 krs = rows_rsrc(p.k8 + kvh, p.Nkp * D);
@@ -729,6 +720,7 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
         (rotated ? (float)pr.d : 1.0f);
   p.qsign = pr.scale < 0.f ? 0x80808080u : 0u;
   constexpr int NW = 4;
+  static_assert(NW == lanes::kFp8Waves, "shared lane layout");
   p.nqb = (pr.Nq + kWR * NW - 1) / (kWR * NW);
   p.total = pr.B * pr.Hq * p.nqb;
   if (pr.d == 128)

@@ -117,6 +117,12 @@ struct Cfg {
   static constexpr int KS = D / 16;  // k-steps of the S^T product
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static_assert(kKT * KSLOTS % 64 == 0 && kKT * VSLOTS % 64 == 0, "split");
+  static_assert(KSLOTS == lanes::prefill_k_chunks(D) &&
+                    VSLOTS == lanes::prefill_v_chunks(D) &&
+                    KLOADS == lanes::prefill_k_loads(D) &&
+                    VLOADS == lanes::prefill_v_loads(D) &&
+                    NW == lanes::kPrefillWaves && kKT == lanes::kTileRows,
+                "tile loads as the shared lane layout states them");
   static_assert(KLW + VLW <= 4 * DB, "interleaved loads fit the PV product");
   // two workgroups per CU: K and V rings and the 1 KB load sink of each fit
   // in half of the 160 KB of LDS
@@ -126,11 +132,7 @@ struct Cfg {
 // Key held in row r of the K tile in LDS.  Rows are in MFMA row order: with
 // this order the 32x32 accumulator of S^T gives lane group g (lanes 32g ..
 // 32g+31) the 16 consecutive keys g*16 .. g*16+15 of each 32-key block.
-__device__ inline int k_row_key(int r) {
-  const int mb = r >> 5;
-  const int rho = r & 31;
-  return mb * 32 + ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3);
-}
+__device__ inline int k_row_key(int r) { return lanes::mfma_row(r); }
 
 // Waits until at most n vector-memory loads of this wave are outstanding
 // (the direct-to-LDS loads count there); the other counters are left alone.
@@ -360,25 +362,16 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   // as zeros, so padded contents never enter LDS.
   unsigned kvo[C::KLW], vvo[C::VLW];
 #pragma unroll
-  for (int m = 0; m < C::KLW; ++m) {
-    const int slot16 = (wave + NW * m) * 64 + lane;
-    const int r = slot16 / C::KSLOTS;
-    const int c = slot16 - r * C::KSLOTS;
-    kvo[m] = 2u * (k_row_key(r) * D + (c < D / 8 ? c * 8 : 0));
-  }
+  for (int m = 0; m < C::KLW; ++m)
+    kvo[m] = lanes::prefill_k_src(D, wave + NW * m, lane);
 #pragma unroll
-  for (int m = 0; m < C::VLW; ++m) {
-    const int slot16 = (wave + NW * m) * 64 + lane;
-    const int r = slot16 / C::VSLOTS;
-    const int c = slot16 - r * C::VSLOTS;
-    vvo[m] = 2u * (r * D + (c < D / 8 ? c * 8 : 0));
-  }
+  for (int m = 0; m < C::VLW; ++m)
+    vvo[m] = lanes::prefill_v_src(D, wave + NW * m, lane);
   // resource of tile t of K or V (`live`: a tile of the plan; otherwise an
   // empty range, whose reads touch no memory)
   auto tile_rsrc = [&](const uint16_t* base, int t, bool live) {
-    const int rows = live ? max(0, min(kKT, L - t * kKT)) : 0;
     return dev::rows_rsrc(live ? base + (size_t)t * kKT * D : base,
-                          rows * D * 2);
+                          lanes::prefill_tile_bytes(D, L, t, live));
   };
   // Interleaved loads (issued during X): every wave issues KLW + VLW of
   // them per tile.  A wave without a load number m (uneven split) writes
