@@ -54,8 +54,8 @@ MUTANTS = {
     "prefill_v_pad_past_row": ("(unsigned)(r * D + (c < D / 8 ? c * 8 : 0)",
                                "(unsigned)(r * D + (c < D / 8 + 4 ? c * 8 : 0)"),
     # a tile's resource not clamped to the valid length
-    "prefill_rsrc_unclamped": ("int rows = live ? L - t * kTileRows : 0;",
-                               "int rows = live ? kTileRows : 0;"),
+    "prefill_rsrc_unclamped": ("const int rows = rem - over;",
+                               "const int rows = rem;"),
     # a chunk permutation wider than the row (d=128 rows have 16 chunks)
     "bwd_swz_past_row": ("return D == 128 ? 4 * (r & 3) +",
                          "return D == 128 ? 8 * (r & 3) +"),

@@ -343,20 +343,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     for (int db = 0; db < C::DB; ++db)
       toff[half][db] = tr_off<D>(lane, half, db);
 
-  // loads of step u (query head hk*G + u / nt, tile t0 + u % nt) into slot S
-  // this wave's loads of a step: wave load u2 = wave + NW*m; u2 < LOADS is
-  // a Q tile load, then dO tile loads, then lse and delta (64 floats each);
-  // per-lane source offsets within a tile are the same every step
+  // loads of step u (query head hk*G + u % G, tile t_last - u / G) into
+  // slot S.  A tile takes LOADS wave-wide loads, dealt round-robin: wave w
+  // issues loads w, w + NW, ... (LOADS is a multiple of NW, so every wave
+  // issues LOADS / NW of the Q tile and as many of the dO tile, at the same
+  // per-lane offsets); waves 0 and 1 also load the tile's lse and delta (64
+  // floats each).  Each load's kind is fixed at compile time.
+  static_assert(C::LOADS % NW == 0 && NW >= 2, "loads per wave");
+  constexpr int TW = C::LOADS / NW;  // tile loads per wave and tile
   constexpr int NL = 2 * C::LOADS + 2;
-  constexpr int LW = (NL + NW - 1) / NW;
-  unsigned toffs[LW];
+  unsigned toffs[TW];
 #pragma unroll
-  for (int m = 0; m < LW; ++m) {
-    const int u2 = wave + NW * m;
-    toffs[m] = u2 < C::LOADS       ? tile_src_off<D>(u2, lane)
-               : u2 < 2 * C::LOADS ? tile_src_off<D>(u2 - C::LOADS, lane)
-                                   : (unsigned)(lane * 4);
-  }
+  for (int m = 0; m < TW; ++m) toffs[m] = tile_src_off<D>(wave + NW * m, lane);
   const int qbytes = s.Lq * D * 2;  // rows past the live rows read zeros
   auto issue = [&](auto slot_c, int u) {
     const int h = hk * p.G + u % p.G;
@@ -367,24 +365,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     const auto ors = rows_rsrc(p.dout + bh * p.Nq * D, qbytes);
     const int tb = r0 * D * 2;
 #pragma unroll
-    for (int m = 0; m < LW; ++m) {
-      const int u2 = wave + NW * m;
-      if (u2 < C::LOADS) {
-        miattn_buffer_load_lds(
-            qrs, (lds_void*)(qslot(slot_c) + u2 * 512), 16, toffs[m] + tb, 0,
-            0, 0);
-      } else if (u2 < 2 * C::LOADS) {
-        miattn_buffer_load_lds(
-            ors, (lds_void*)(oslot(slot_c) + (u2 - C::LOADS) * 512), 16,
-            toffs[m] + tb, 0, 0, 0);
-      } else if (u2 < NL) {
-        const bool isl = u2 == 2 * C::LOADS;
-        const auto rs =
-            rows_rsrc((isl ? p.lse2 : p.delta) + bh * p.Nqp, p.Nqp * 4);
-        miattn_buffer_load_lds(
-            rs, (lds_void*)(isl ? lslot(slot_c) : dslot(slot_c)), 4,
-            toffs[m] + r0 * 4, 0, 0, 0);
-      }
+    for (int m = 0; m < TW; ++m)
+      miattn_buffer_load_lds(
+          qrs, (lds_void*)(qslot(slot_c) + (wave + NW * m) * 512), 16,
+          toffs[m] + tb, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < TW; ++m)
+      miattn_buffer_load_lds(
+          ors, (lds_void*)(oslot(slot_c) + (wave + NW * m) * 512), 16,
+          toffs[m] + tb, 0, 0, 0);
+    if (wave < 2) {
+      const bool isl = wave == 0;
+      const auto rs =
+          rows_rsrc((isl ? p.lse2 : p.delta) + bh * p.Nqp, p.Nqp * 4);
+      miattn_buffer_load_lds(
+          rs, (lds_void*)(isl ? lslot(slot_c) : dslot(slot_c)), 4,
+          (unsigned)(lane * 4) + r0 * 4, 0, 0, 0);
     }
   };
 
@@ -710,31 +706,28 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       toff[half][db] = tr_off<D>(lane, half, db);
 
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
-  // this wave's tile loads: wave load u2 = wave + NW*m, K tile loads first
-  constexpr int NL = 2 * C::LOADS;
-  constexpr int LW = (NL + NW - 1) / NW;
-  unsigned toffs[LW];
+  // this wave's tile loads: wave w issues loads w, w + NW, ... of the K tile
+  // and the same of the V tile (LOADS is a multiple of NW), at the same
+  // per-lane offsets
+  static_assert(C::LOADS % NW == 0, "loads per wave");
+  constexpr int TW = C::LOADS / NW;
+  unsigned toffs[TW];
 #pragma unroll
-  for (int m = 0; m < LW; ++m) {
-    const int u2 = wave + NW * m;
-    toffs[m] = tile_src_off<D>(u2 < C::LOADS ? u2 : u2 - C::LOADS, lane);
-  }
+  for (int m = 0; m < TW; ++m) toffs[m] = tile_src_off<D>(wave + NW * m, lane);
   const auto krs = rows_rsrc(p.k + kv_base, s.L * D * 2);
   const auto vrs = rows_rsrc(p.v + kv_base, s.L * D * 2);
   auto issue = [&](auto slot_c, int u) {
     const int tb = tile_of(u) * kRT * D * 2;
 #pragma unroll
-    for (int m = 0; m < LW; ++m) {
-      const int u2 = wave + NW * m;
-      if (u2 < C::LOADS)
-        miattn_buffer_load_lds(
-            krs, (lds_void*)(kslot(slot_c) + u2 * 512), 16, toffs[m] + tb, 0,
-            0, 0);
-      else if (u2 < NL)
-        miattn_buffer_load_lds(
-            vrs, (lds_void*)(vslot(slot_c) + (u2 - C::LOADS) * 512), 16,
-            toffs[m] + tb, 0, 0, 0);
-    }
+    for (int m = 0; m < TW; ++m)
+      miattn_buffer_load_lds(
+          krs, (lds_void*)(kslot(slot_c) + (wave + NW * m) * 512), 16,
+          toffs[m] + tb, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < TW; ++m)
+      miattn_buffer_load_lds(
+          vrs, (lds_void*)(vslot(slot_c) + (wave + NW * m) * 512), 16,
+          toffs[m] + tb, 0, 0, 0);
   };
 
   auto compute = [&](auto slot_c, int u) {

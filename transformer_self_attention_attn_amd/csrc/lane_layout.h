@@ -60,10 +60,13 @@ MIATTN_HD constexpr unsigned prefill_v_src(int D, int i, int lane) {
 }
 // Bytes of tile t's resource: its rows below the valid length L (0 for a
 // step past the plan), starting at the tile.
+// (Written without a plain clamp, which the device compiler turns into a
+// vector med3 and a readfirstlane; this form stays on the scalar unit.)
 MIATTN_HD constexpr int prefill_tile_bytes(int D, int L, int t, bool live) {
-  int rows = live ? L - t * kTileRows : 0;
-  rows = rows < 0 ? 0 : (rows > kTileRows ? kTileRows : rows);
-  return rows * D * 2;
+  const int rem = L - t * kTileRows;  // rows of the sequence from the tile on
+  const int over = rem > kTileRows ? rem - kTileRows : 0;
+  const int rows = rem - over;        // min(rem, 64)
+  return live && rows > 0 ? rows * D * 2 : 0;
 }
 
 // ---- backward (bf16) ------------------------------------------------------

@@ -167,10 +167,15 @@ __device__ inline void barrier_nofence() {
 // x of the upper half in every lane.  Written as inline assembly with two
 // distinct registers: the builtin given the same value twice was folded to
 // a single result.
+// The maximum is taken inside the same block, so the compiler does not
+// canonicalize the two swapped values before it (they are never NaN).
 __device__ inline float half_swap_max(float x) {
   float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
+  asm volatile(
+      "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(a), "+v"(b));
+  return a;
 }
 
 struct PrefillParams {
@@ -588,9 +593,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
       }
       return a;
     };
-    float mn2[2] = {-INFINITY, -INFINITY};
-    // row sum of this tile's weights in fp32 (lse needs the exact sum)
-    float l2[2] = {0.f, 0.f};
+    // two partial maxima and sums, each started from its first element
+    float mn2[2], l2[2];
     bf16x8 va[5];
 #pragma unroll
     for (int i = 0; i < 4; ++i) va[i] = vread(i);
@@ -609,13 +613,16 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
 #pragma unroll
       for (int u = 0; u < 32 / NPV; ++u) {
         const int el = i * (32 / NPV) + u;
-        mn2[u & 1] = fmaxf(mn2[u & 1], sn[el >> 4][el & 15]);
+        const float x = sn[el >> 4][el & 15];
+        mn2[el & 1] = el < 2 ? x : fmaxf(mn2[el & 1], x);
       }
-      // the 32 weights of this lane, 32 / NPV of them per MFMA slot
+      // the 32 weights of this lane (the row sum in fp32: lse needs the
+      // exact sum), 32 / NPV of them per MFMA slot
 #pragma unroll
       for (int u = 0; u < 32 / NPV; ++u) {
         const int el = i * (32 / NPV) + u;
-        l2[u & 1] += sc[el >> 4][el & 15];
+        const float x = sc[el >> 4][el & 15];
+        l2[el & 1] = el < 2 ? x : l2[el & 1] + x;
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
