@@ -671,6 +671,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 
   // Q and dO of this lane's row as B operands; lse and delta of the row
   const size_t bh = (size_t)b * p.Hq + h;
+  // S c is formed with c > 0 (the mask relies on -inf c = -inf): for a
+  // negative scale Q is negated on load (its only use is S) and c flipped;
+  // scale 0 takes a tiny positive c, under which every allowed pair weighs
+  // the same
+  const bool qneg = p.c < 0.f;
+  const float cc = qneg ? -p.c : (p.c > 0.f ? p.c : 1e-30f);
+  const unsigned qsign = qneg ? 0x80008000u : 0u;
   bf16x8 qf[C::KS], of[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
@@ -681,6 +688,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       c = *reinterpret_cast<const u32x4*>(p.dout + (bh * p.Nq + qi) * D +
                                           16 * ks + 8 * g);
     }
+    a ^= qsign;
     qf[ks] = __builtin_bit_cast(bf16x8, a);
     of[ks] = __builtin_bit_cast(bf16x8, c);
   }
@@ -736,47 +744,55 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const uint16_t* Kt = kslot(slot_c);
     const uint16_t* Vt = vslot(slot_c);
     // S^T = K Q^T and dP^T = V dO^T: lane (query, g) holds keys
-    // mb*32 + 16g + r of the tile
-    f32x16 sa[2], pa[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sa[mb][r] = 0.f;
-        pa[mb][r] = 0.f;
-      }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Kt + aoff[mb][ks]);
-        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sa[mb], 0,
-                                                         0, 0);
-      }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Vt + aoff[mb][ks]);
-        pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[ks], pa[mb], 0,
-                                                         0, 0);
-      }
-    const bool full = tile_full(t);
+    // mb*32 + 16g + r of the tile.  On a tile that needs the mask, S^T
+    // starts from -inf at the pairs the mask excludes (else from 0): with
+    // c > 0 their P is then exactly 0.
     const int j0 = t * kRT;
+    f32x16 sa[2], pa[2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sa[mb] = zero;
+    if (!tile_full(t)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = j0 + mb * 32 + 16 * g + r;
+          const bool ok =
+              (jj < rk.hc) & (((jj >= rk.lo) & (jj < rk.hw)) | (jj < rk.sk));
+          sa[mb][r] = ok ? 0.f : -INFINITY;
+        }
+    }
+    // the 4 KS MFMAs (ks, mb, S^T or dP^T), each A operand read from LDS
+    // two MFMAs ahead
+    constexpr int NS = 4 * C::KS;
+    auto fetch = [&](auto i_c) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int ks = i / 4, mb = (i / 2) % 2;
+      return *reinterpret_cast<const bf16x8*>((i % 2 == 0 ? Kt : Vt) +
+                                              aoff[mb][ks]);
+    };
+    bf16x8 ring[3];
+    ring[0] = fetch(ic<0>());
+    ring[1] = fetch(ic<1>());
+    static_for<0, NS>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int ks = i / 4, mb = (i / 2) % 2;
+      if constexpr (i + 2 < NS) ring[(i + 2) % 3] = fetch(ic<i + 2>());
+      if constexpr (i % 2 == 0)
+        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % 3], qf[ks],
+                                                         sa[mb], 0, 0, 0);
+      else
+        pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ring[i % 3], of[ks], ks == 0 ? zero : pa[mb], 0, 0, 0);
+    });
     bf16x8 sb[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l2));
-        if (!full) {
-          const int jj = j0 + mb * 32 + 16 * g + r;
-          if (jj >= rk.hc || ((jj < rk.lo || jj >= rk.hw) && jj >= rk.sk))
-            pr = 0.f;
-        }
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], cc, -l2));
         dsv[r] = pr * (pa[mb][r] + ndl);
       }
 #pragma unroll
