@@ -786,37 +786,53 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
         pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             ring[i % 3], of[ks], ks == 0 ? zero : pa[mb], 0, 0, 0);
     });
+    // dS^T = P (dP - delta) of keys 32 mb + 16 g + r, in bf16
     bf16x8 sb[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], cc, -l2));
-        dsv[r] = pr * (pa[mb][r] + ndl);
-      }
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
+    float dsv[16];
+    auto element = [&](auto mb_c, auto r_c) __attribute__((always_inline)) {
+      constexpr int mb = decltype(mb_c)::value, r = decltype(r_c)::value;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], cc, -l2));
+      dsv[r] = pr * (pa[mb][r] + ndl);
+      if constexpr (r % 8 == 7) {
+        constexpr int m2 = r / 8;
         f32x8 y;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = dsv[8 * m2 + e];
         sb[mb][m2] = __builtin_convertvector(y, bf16x8);
       }
-    }
-    // dQ^T += K^T dS^T over the tile's 64 keys
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        const int c0 = (32 * mb + 8 * m2) * D;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a =
-              tr_pair(Kt + toff[0][db] + c0, Kt + toff[1][db] + c0 + 4 * D);
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
-                                                            dqa[db], 0, 0, 0);
-        }
+    };
+    static_for<0, 16>([&](auto r_c) __attribute__((always_inline)) {
+      element(ic<0>(), r_c);
+    });
+    // dQ^T += K^T dS^T over the tile's 64 keys (4 DB MFMAs, (mb, m2, db)),
+    // A operands read two MFMAs ahead; the dS^T of keys 32 .. 63 is formed
+    // between the MFMAs over keys 0 .. 31
+    constexpr int NQ = 4 * C::DB;
+    auto fetch_q = [&](auto i_c) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int mb = i / (2 * C::DB), m2 = (i / C::DB) % 2,
+                    db = i % C::DB;
+      constexpr int c0 = (32 * mb + 8 * m2) * D;
+      return tr_pair(Kt + toff[0][db] + c0, Kt + toff[1][db] + c0 + 4 * D);
+    };
+    bf16x8 qring[3];
+    qring[0] = fetch_q(ic<0>());
+    qring[1] = fetch_q(ic<1>());
+    static_for<0, NQ>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int mb = i / (2 * C::DB), m2 = (i / C::DB) % 2,
+                    db = i % C::DB;
+      if constexpr (i + 2 < NQ) qring[(i + 2) % 3] = fetch_q(ic<i + 2>());
+      dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qring[i % 3],
+                                                        sb[mb][m2], dqa[db], 0,
+                                                        0, 0);
+      if constexpr (i < NQ / 2) {
+        static_for<i * 32 / NQ, (i + 1) * 32 / NQ>(
+            [&](auto r_c) __attribute__((always_inline)) {
+              element(ic<1>(), r_c);
+            });
       }
+    });
   };
 
   if (nt > 0) {
