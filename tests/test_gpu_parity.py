@@ -39,6 +39,10 @@ PREFILL_CASES = [
     W("gqa4-d128-window100-padded", 2, 8, 2, 515, 515, 128, "bf16", True,
       window=100, len_lo=60, len_hi=515),
     W("amp3-d128-causal", 1, 2, 1, 200, 200, 128, "bf16", True, amp=3.0),
+    # longer d=64 rows: dead rows, lengths from 1 key, a ragged last tile
+    W("d64-long-causal-padded", 3, 4, 2, 777, 777, 64, "bf16", True,
+      len_lo=1, len_hi=777),
+    W("d64-long-nocausal", 2, 2, 1, 1000, 1000, 64, "bf16", False),
 ]
 
 
@@ -352,8 +356,13 @@ def test_v_ones_gives_ones():
     assert (o.float()[~live] == 0).all()
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_dominant_key_anywhere_in_a_tile(d):
+@pytest.mark.parametrize("d,N,pos", [
+    (64, 256, [40, 100, 200, 255]),
+    (128, 256, [40, 100, 200, 255]),
+    # 1024 keys at d=64: the key early and late in long rows
+    (64, 1024, [40, 300, 700, 1000]),
+], ids=["d64", "d128", "d64-long"])
+def test_dominant_key_anywhere_in_a_tile(d, N, pos):
     """One key dominates every query's scores by about 200 (log2 units), far
     past the lazy-rescale threshold and past what fp32 can hold as an
     unshifted weight, so the running maximum must see it wherever it sits.
@@ -361,8 +370,7 @@ def test_dominant_key_anywhere_in_a_tile(d):
     32-key halves of a tile.  The output must be that key's V row and lse its
     score (the oracle's exact values)."""
     import oracle
-    B, H, N = 4, 2, 256
-    pos = [40, 100, 200, 255]
+    B, H = 4, 2
     g = torch.Generator().manual_seed(7)
     u = torch.ones(d) / math.sqrt(d)
     amp = math.sqrt(140.0 * math.sqrt(d))  # dominant score amp^2 / sqrt(d)
