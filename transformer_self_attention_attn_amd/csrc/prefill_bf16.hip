@@ -186,6 +186,7 @@ struct PrefillParams {
   float* lse;
   const int* seqlens;
   int B, Hq, Hkv, Nq, Nk, G, nqb, causal, window, window_right, sinks, total;
+  int qband;       // query blocks per band of the causal block order
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
 };
@@ -222,7 +223,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   // when the groups divide evenly over the XCDs, each XCD runs its blocks
   // heaviest first across all of its groups (longest job first), so that no
   // long diagonal block starts late; otherwise heaviest first within each
-  // group.
+  // group.  Where a group's K/V is large, the heaviest-first order goes band
+  // by band (qband query blocks each, enough blocks to fill the XCD's
+  // slots), one group at a time within a band, so that the XCD's L2 mostly
+  // holds one group's K/V.
   const int n = p.total;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
@@ -231,10 +235,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   int grp, qrank, hh;
   if (p.causal && ngrp % kXcds == 0) {
     const int gpx = ngrp / kXcds;  // groups per XCD
-    qrank = slot / (gpx * p.G);
-    const int r1 = slot - qrank * gpx * p.G;
-    grp = xcd * gpx + r1 / p.G;
-    hh = r1 - (r1 / p.G) * p.G;
+    const int bs = p.qband * p.G;  // blocks of one group in a band
+    const int band = slot / (gpx * bs);
+    const int r1 = slot - band * gpx * bs;
+    const int gi = r1 / bs;
+    const int r2 = r1 - gi * bs;
+    qrank = band * p.qband + r2 / p.G;
+    grp = xcd * gpx + gi;
+    hh = r2 - (r2 / p.G) * p.G;
   } else {
     const int per = n / kXcds;
     const int rem = n % kXcds;
@@ -718,6 +726,19 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
   PrefillParams p = p0;
   p.nqb = (p.Nq + C::QB - 1) / C::QB;
   p.total = p.B * p.Hq * p.nqb;
+  // bands of the causal block order: with 1 MB of K/V or more per group,
+  // the smallest divisor of nqb whose band of one group (qband * G blocks)
+  // fills an XCD's workgroup slots (32 CUs); otherwise 1 (plain heaviest
+  // first across the XCD's groups)
+  p.qband = 1;
+  if (2LL * p.Nk * D * 2 >= (1LL << 20)) {
+    const int slots = 32 * (D == 64 ? 3 : 2);
+    for (int qb = 1; qb <= p.nqb; ++qb)
+      if (p.nqb % qb == 0) {
+        p.qband = qb;
+        if (qb * p.G >= slots) break;
+      }
+  }
   hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
 }
