@@ -109,72 +109,114 @@ struct QuantParams {
   int mode;            // 0: block scale; 1: amax only; 2: preset amax
 };
 
+// Up to three tensors quantized by one launch: blocks [first[i], first[i+1])
+// (first[3] = the grid) belong to tensor i.
+struct QuantSet {
+  QuantParams t[3];
+  int first[4];
+};
+
+// x of the lane whose index differs from this one's in bit LB (LB = 1, 2,
+// 4, 8): DPP quad permutations for 1 and 2, a rotation by 8 within the
+// 16-lane row for 8 (the same pairing), a swizzle for 4.
+template <int LB>
+__device__ inline float lane_xor(float x) {
+  const int i = __float_as_int(x);
+  int r;
+  if constexpr (LB == 1)
+    r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+  else if constexpr (LB == 2)
+    r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+  else if constexpr (LB == 8)
+    r = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, true);  // row_ror:8
+  else
+    r = __builtin_amdgcn_ds_swizzle(i, 0x1F | (LB << 10));  // xor LB
+  return __int_as_float(r);
+}
+
 // mode 0: codes and scale from the block's own amax; mode 1: writes the
 // block's amax to scales[] and nothing else; mode 2: reads amax from
 // scales[] (all blocks of the tensor set to one value), writes codes and the
 // scale amax / 448.
+// Layout of the work: a workgroup of 4 waves takes one block of 64 rows,
+// 16 rows a wave.  A row is D / 8 lanes of 8 values (16-byte loads, so one
+// wave instruction reads RPI whole rows); the butterflies of width 1, 2 and 4
+// stay inside a lane, those of width 8 .. D/2 pair lanes of the same row.
+// The levels run in the same order (width 1 first) as one lane holding a
+// whole row would run them, so every value goes through the same float32
+// operations.
 template <int D>
-__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantParams p) {
-  constexpr int E = D / 64;  // values per lane of a row
+__global__ __launch_bounds__(256) void fp8_quant_kernel(QuantSet set) {
+  constexpr int LPR = D / 8;     // lanes per row
+  constexpr int RPI = 64 / LPR;  // rows per wave instruction
+  constexpr int NI = 16 / RPI;   // instructions for a wave's 16 rows
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlk];
-  const int blk = blockIdx.x % p.nblk;
-  const int bh = blockIdx.x / p.nblk;
+  const int bid = blockIdx.x;
+  const int ti = bid >= set.first[2] ? 2 : (bid >= set.first[1] ? 1 : 0);
+  const QuantParams& p = set.t[ti];
+  const int lbid = bid - set.first[ti];
+  const int blk = lbid % p.nblk;
+  const int bh = lbid / p.nblk;
   const int b = bh / p.H;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int sub = lane / LPR;  // row of the instruction's group
+  const int cl = lane % LPR;   // 8-value chunk of the row
   const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
   const int valid = p.is_q ? s.Lq : s.L;
   const int r0 = blk * kBlk;
 
-  float sg[E];
+  float sg[8];
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    sg[e] = p.signs ? (float)p.signs[lane * E + e] : 1.0f;
+  for (int e = 0; e < 8; ++e)
+    sg[e] = p.signs ? (float)p.signs[cl * 8 + e] : 1.0f;
 
-  // rows r0 + wave*16 .. +15 of the block: load, rotate, track |max|
-  float v[16][E];
+  // rows r0 + wave*16 + i*RPI + sub: load, rotate, track |max|
+  float v[NI][8];
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + wave * 16 + i;
+  for (int i = 0; i < NI; ++i) {
+    const int r = r0 + wave * 16 + i * RPI + sub;
     const bool ok = r < valid && r < p.N;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (ok)
+      raw = *reinterpret_cast<const u32x4*>(p.x + ((size_t)bh * p.N + r) * D +
+                                            cl * 8);
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[i][e] = 0.f;
-    if (ok) {
-      const uint16_t* src = p.x + ((size_t)bh * p.N + r) * D + lane * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        v[i][e] = __uint_as_float((unsigned)src[e] << 16);
+    for (int w = 0; w < 4; ++w) {
+      v[i][2 * w] = __uint_as_float(raw[w] << 16);
+      v[i][2 * w + 1] = __uint_as_float(raw[w] & 0xffff0000u);
     }
     if (p.signs) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[i][e] *= sg[e];
+      for (int e = 0; e < 8; ++e) v[i][e] *= sg[e];
       // butterflies of width h: element j pairs with j ^ h; the lower one
       // becomes a + b, the upper one a - b
 #pragma unroll
-      for (int h = 1; h < D; h <<= 1) {
-        if (h < E) {
+      for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            if ((e & h) == 0) {
-              const float a = v[i][e], c = v[i][e + h];
-              v[i][e] = a + c;
-              v[i][e + h] = a - c;
-            }
-        } else {
-          const int lb = h / E;  // partner lane differs in this bit
-          const bool upper = (lane & lb) != 0;
+        for (int e = 0; e < 8; ++e)
+          if ((e & h) == 0) {
+            const float a = v[i][e], c = v[i][e + h];
+            v[i][e] = a + c;
+            v[i][e + h] = a - c;
+          }
+      // widths 8 .. D/2: the partner lane (same row) differs in bit h / 8
+      static_for<0, 5>([&](auto k_c) {
+        constexpr int LB = 1 << decltype(k_c)::value;
+        if constexpr (8 * LB < D) {
+          const bool upper = (cl & LB) != 0;
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float o = __shfl_xor(v[i][e], lb);
+          for (int e = 0; e < 8; ++e) {
+            const float o = lane_xor<LB>(v[i][e]);
             v[i][e] = upper ? o - v[i][e] : v[i][e] + o;
           }
         }
-      }
+      });
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
   }
   amax = wave_maxf(amax);
   if (lane == 0) red[wave] = amax;
@@ -192,28 +234,28 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(QuantParams p) {
   const float mul = amax > 0.f ? kE4M3Max / amax : 0.f;
   if (threadIdx.x == 0) *sp = amax / kE4M3Max;
 
-  // codes: row-major rows, or through LDS into the transposed tile
+  // codes: 8 bytes a lane and row, row-major, or through LDS into the
+  // transposed tile
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rl = wave * 16 + i;
+  for (int i = 0; i < NI; ++i) {
+    const int rl = wave * 16 + i * RPI + sub;
     const int r = r0 + rl;
-    unsigned w = 0;
-    if constexpr (E == 2) {
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] * mul, v[i][1] * mul, 0u,
-                                          false);
-    } else {
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][0] * mul, 0.f, 0u, false);
+    unsigned w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w[h] = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4 * h] * mul,
+                                             v[i][4 * h + 1] * mul, 0u, false);
+      w[h] = __builtin_amdgcn_cvt_pk_fp8_f32(v[i][4 * h + 2] * mul,
+                                             v[i][4 * h + 3] * mul, w[h], true);
     }
     if (p.transposed) {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        tile[(lane * E + e) * kBlk + rl] = (uint8_t)(w >> (8 * e));
+      for (int e = 0; e < 8; ++e)
+        tile[(cl * 8 + e) * kBlk + rl] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
     } else if (r < p.Npad) {
-      uint8_t* dst = p.codes + ((size_t)bh * p.Npad + r) * D + lane * E;
-      if constexpr (E == 2)
-        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w & 0xffffu);
-      else
-        *dst = (uint8_t)(w & 0xffu);
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      uint8_t* dst = p.codes + ((size_t)bh * p.Npad + r) * D + cl * 8;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
     }
   }
   if (p.transposed) {
@@ -619,19 +661,35 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
 }
 
 template <int D>
-hipError_t quant_one(QuantParams q, hipStream_t st, bool per_tensor) {
-  const unsigned grid = (unsigned)(q.B * q.H * q.nblk);
-  if (!per_tensor) {
-    q.mode = 0;
-    hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
-    return hipGetLastError();
-  }
-  q.mode = 1;
-  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
+hipError_t quant_one(QuantParams q, hipStream_t st) {
+  const int grid = q.B * q.H * q.nblk;
+  QuantSet set = {};
+  set.t[0] = q;
+  set.first[1] = set.first[2] = set.first[3] = grid;
+  set.t[0].mode = 1;
+  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, set);
   hipLaunchKernelGGL(fp8_tensor_amax_kernel, dim3(1), dim3(256), 0, st,
-                     q.scales, (int)grid);
-  q.mode = 2;
-  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, q);
+                     q.scales, grid);
+  set.t[0].mode = 2;
+  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(grid), dim3(256), 0, st, set);
+  return hipGetLastError();
+}
+
+// Block scales: Q, K and V in one launch.
+template <int D>
+hipError_t quant_three(const QuantParams& a, const QuantParams& k,
+                       const QuantParams& v, hipStream_t st) {
+  QuantSet set = {};
+  set.t[0] = a;
+  set.t[1] = k;
+  set.t[2] = v;
+  set.first[0] = 0;
+  set.first[1] = a.B * a.H * a.nblk;
+  set.first[2] = set.first[1] + k.B * k.H * k.nblk;
+  set.first[3] = set.first[2] + v.B * v.H * v.nblk;
+  for (int i = 0; i < 3; ++i) set.t[i].mode = 0;
+  hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3(set.first[3]), dim3(256), 0,
+                     st, set);
   return hipGetLastError();
 }
 
@@ -680,15 +738,17 @@ hipError_t launch_fp8_quantize(const void* q, const void* k, const void* v,
   c.signs = nullptr;
   c.transposed = 1;
   hipError_t e;
-  const bool pt = per_tensor != 0;
+  if (!per_tensor)
+    return pr.d == 128 ? quant_three<128>(a, bk, c, stream)
+                       : quant_three<64>(a, bk, c, stream);
   if (pr.d == 128) {
-    if ((e = quant_one<128>(a, stream, pt)) != hipSuccess) return e;
-    if ((e = quant_one<128>(bk, stream, pt)) != hipSuccess) return e;
-    return quant_one<128>(c, stream, pt);
+    if ((e = quant_one<128>(a, stream)) != hipSuccess) return e;
+    if ((e = quant_one<128>(bk, stream)) != hipSuccess) return e;
+    return quant_one<128>(c, stream);
   }
-  if ((e = quant_one<64>(a, stream, pt)) != hipSuccess) return e;
-  if ((e = quant_one<64>(bk, stream, pt)) != hipSuccess) return e;
-  return quant_one<64>(c, stream, pt);
+  if ((e = quant_one<64>(a, stream)) != hipSuccess) return e;
+  if ((e = quant_one<64>(bk, stream)) != hipSuccess) return e;
+  return quant_one<64>(c, stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
