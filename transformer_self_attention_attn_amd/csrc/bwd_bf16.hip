@@ -43,9 +43,12 @@
 // read, the A operand of dO^T P); tiles are stored unpadded with the 16-byte
 // chunks of each row permuted by an XOR of row bits (see swz), which keeps
 // both kinds of read free of LDS bank conflicts.
-// The dK/dV step runs its 64 MFMAs (d=128) from a ring of operands read four
-// MFMAs ahead, and the softmax of one 32-row half of the tile runs between
-// the MFMAs of the other half.
+// The dK/dV step reads its MFMA operands from a ring four MFMAs ahead.  At
+// d=64 the step is one sequence of MFMAs in which the softmax of one 32-row
+// half of the tile runs between the MFMAs of the other half; at d=128 the
+// halves pass through a three-stream pipeline (products of the next half,
+// softmax of this one, gradient products of the previous one), so that the
+// exponentials spread over every MFMA of the step.
 #include "kernels.h"
 
 #include <cmath>
@@ -206,7 +209,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // bwd_dkdv
 
-template <int D, int NW>
+// PIPE: the step runs as the three-stream pipeline described below (d=128);
+// otherwise as one sequence of MFMAs per tile (d=64, whose workgroups walk
+// few tiles: the pipeline's fill and drain and the fully masked tiles it
+// computes cost more there than it gains).
+template <int D, int NW, bool PIPE>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     BwdParams p) {
   using C = BCfg<D>;
@@ -272,10 +279,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   int rlo, rhi;
   key_rows(j, rlo, rhi);
   const bool kne = rlo < rhi;
-  const int w_lo_min = wave_imin(kne ? rlo : kBig);
-  const int w_hi_max = wave_imax(kne ? rhi : -kBig);
-  const int w_lo_max = wave_imax(rlo);
-  const int w_hi_min = wave_imin(rhi);
+  // (wave-uniform; the pipelined step reads them back as scalars, so that
+  // its tests are scalar branches)
+  auto uni = [](int x) { return PIPE ? __builtin_amdgcn_readfirstlane(x) : x; };
+  const int w_lo_min = uni(wave_imin(kne ? rlo : kBig));
+  const int w_hi_max = uni(wave_imax(kne ? rhi : -kBig));
+  const int w_lo_max = uni(wave_imax(rlo));
+  const int w_hi_min = uni(wave_imin(rhi));
   // the workgroup's hull: the lowest key's first row and, unless the block
   // holds a sink key, the last valid key's end row
   int t0 = 0, nt = 0;
@@ -307,6 +317,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   // K and V of this lane's key as B operands (8 consecutive columns per
   // k-step), zero past the valid length
   const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Nk * D;
+  // The pipelined step forms S c with c > 0 (its mask relies on
+  // -inf c = -inf): for a negative scale K is negated on load (its only use
+  // is S) and c flipped; scale 0 takes a tiny positive c, under which every
+  // allowed pair weighs the same.  The other step masks explicitly and
+  // takes c as it is.
+  const bool kneg = PIPE && p.c < 0.f;
+  const float cc = !PIPE ? p.c : kneg ? -p.c : (p.c > 0.f ? p.c : 1e-30f);
+  const unsigned ksign = kneg ? 0x80008000u : 0u;
   bf16x8 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
@@ -317,6 +335,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       rv = *reinterpret_cast<const u32x4*>(p.v + kv_base + (size_t)j * D +
                                            16 * ks + 8 * g);
     }
+    rk ^= ksign;
     kf[ks] = __builtin_bit_cast(bf16x8, rk);
     vf[ks] = __builtin_bit_cast(bf16x8, rv);
   }
@@ -384,178 +403,401 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     }
   };
 
-  // One step, as a sequence of NM MFMAs:
-  //   [0, NA)         S = Q K^T and dP = dO V^T of tile rows 0 .. 31
-  //   [NA, 2NA)       the same for rows 32 .. 63, with P and dS of rows
-  //                   0 .. 31 computed in between
-  //   [2NA, 2NA+NB)   dV^T += dO^T P and dK^T += Q^T dS over rows 0 .. 31,
-  //                   with P and dS of rows 32 .. 63 in between
-  //   [2NA+NB, NM)    the same over rows 32 .. 63
-  // Each MFMA's A operand is read from LDS four MFMAs ahead.
-  constexpr int NA = 2 * C::KS;
-  constexpr int NB = 4 * C::DB;
-  constexpr int NM = 2 * NA + 2 * NB;
-  constexpr int AHEAD = 4;
-  constexpr int RING = AHEAD + 1;
-  constexpr int EPS = 16 / NA;  // softmax elements per MFMA slot
-  static_assert(NA == NB && 16 % NA == 0, "slots");
+  if constexpr (!PIPE) {
+    // One step, as a sequence of NM MFMAs:
+    //   [0, NA)         S = Q K^T and dP = dO V^T of tile rows 0 .. 31
+    //   [NA, 2NA)       the same for rows 32 .. 63, with P and dS of rows
+    //                   0 .. 31 computed in between
+    //   [2NA, 2NA+NB)   dV^T += dO^T P and dK^T += Q^T dS over rows 0 .. 31,
+    //                   with P and dS of rows 32 .. 63 in between
+    //   [2NA+NB, NM)    the same over rows 32 .. 63
+    // Each MFMA's A operand is read from LDS four MFMAs ahead.
+    constexpr int NA = 2 * C::KS;
+    constexpr int NB = 4 * C::DB;
+    constexpr int NM = 2 * NA + 2 * NB;
+    constexpr int AHEAD = 4;
+    constexpr int RING = AHEAD + 1;
+    constexpr int EPS = 16 / NA;  // softmax elements per MFMA slot
+    static_assert(NA == NB && 16 % NA == 0, "slots");
 
-  // FULL: every (row, key) pair of the tile is allowed, no mask arithmetic
-  auto compute_t = [&](auto slot_c, auto full_c, int t) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const uint16_t* Qt = qslot(slot_c);
-    const uint16_t* Ot = oslot(slot_c);
-    const float* Lt = lslot(slot_c);
-    const float* Dt = dslot(slot_c);
+    // FULL: every (row, key) pair of the tile is allowed, no mask arithmetic
+    auto compute_t = [&](auto slot_c, auto full_c, int t) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const uint16_t* Qt = qslot(slot_c);
+      const uint16_t* Ot = oslot(slot_c);
+      const float* Lt = lslot(slot_c);
+      const float* Dt = dslot(slot_c);
 
-    auto fetch = [&](auto i_c) -> bf16x8 {
-      constexpr int i = decltype(i_c)::value;
-      if constexpr (i < 2 * NA) {
-        constexpr int mb = i / NA, ks = (i % NA) / 2;
-        const uint16_t* tb = (i % 2 == 0) ? Qt : Ot;
-        return *reinterpret_cast<const bf16x8*>(tb + aoff[mb][ks]);
-      } else {
-        constexpr int x = i - 2 * NA;
-        constexpr int mb = x / NB, r = x % NB;
-        constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
-        const uint16_t* tb = (r % 2 == 0) ? Ot : Qt;
-        constexpr int c0 = (32 * mb + 8 * m2) * D;
-        return tr_pair(tb + toff[0][db] + c0, tb + toff[1][db] + c0 + 4 * D);
-      }
-    };
-
-    f32x16 sa[2], pa[2];
-    bf16x8 pb[2][2], sb[2][2];
-    const f32x16 zero = {};
-    // dP starts from -delta of its rows, so the accumulator ends at
-    // dP - delta (the factor of dS besides P)
-    f32x16 nd0[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 d4 =
-            *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nd0[mb][4 * q4 + e] = d4[e];
-      }
-    auto mfma = [&](auto i_c, const bf16x8& a) {
-      constexpr int i = decltype(i_c)::value;
-      if constexpr (i < 2 * NA) {
-        constexpr int mb = i / NA, ks = (i % NA) / 2;
-        if constexpr (i % 2 == 0)
-          sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, kf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0);
-        else
-          pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, vf[ks], ks == 0 ? nd0[mb] : pa[mb], 0, 0, 0);
-      } else {
-        constexpr int x = i - 2 * NA;
-        constexpr int mb = x / NB, r = x % NB;
-        constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
-        if constexpr (r % 2 == 0)
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][m2],
-                                                            dva[db], 0, 0, 0);
-        else
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
-                                                            dka[db], 0, 0, 0);
-      }
-    };
-
-    // softmax of rows 32 mb + 16 g + r of this tile (lane = key): a row
-    // outside [rlo, rhi) is masked unless the tile is full
-    const int r0 = t * kRT;
-    float pvv[16], dsv[16];
-    f32x4 l4;
-    int mlo[2], mhi[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int base = r0 + mb * 32 + 16 * g;
-      mlo[mb] = rlo - base;
-      mhi[mb] = rhi - base;
-    }
-    auto element = [&](auto mb_c, auto r_c) {
-      constexpr int mb = decltype(mb_c)::value, r = decltype(r_c)::value;
-      if constexpr (r % 4 == 0)
-        l4 = *reinterpret_cast<const f32x4*>(Lt + mb * 32 + 16 * g + r);
-      float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], p.c, -l4[r % 4]));
-      if constexpr (!FULL) pr = (r >= mlo[mb] && r < mhi[mb]) ? pr : 0.f;
-      pvv[r] = pr;
-      dsv[r] = pr * pa[mb][r];
-      if constexpr (r % 8 == 7) {
-        constexpr int m2 = r / 8;
-        f32x8 x, y;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] = pvv[8 * m2 + e];
-          y[e] = dsv[8 * m2 + e];
+      auto fetch = [&](auto i_c) -> bf16x8 {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < 2 * NA) {
+          constexpr int mb = i / NA, ks = (i % NA) / 2;
+          const uint16_t* tb = (i % 2 == 0) ? Qt : Ot;
+          return *reinterpret_cast<const bf16x8*>(tb + aoff[mb][ks]);
+        } else {
+          constexpr int x = i - 2 * NA;
+          constexpr int mb = x / NB, r = x % NB;
+          constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+          const uint16_t* tb = (r % 2 == 0) ? Ot : Qt;
+          constexpr int c0 = (32 * mb + 8 * m2) * D;
+          return tr_pair(tb + toff[0][db] + c0, tb + toff[1][db] + c0 + 4 * D);
         }
-        pb[mb][m2] = __builtin_convertvector(x, bf16x8);
-        sb[mb][m2] = __builtin_convertvector(y, bf16x8);
+      };
+
+      f32x16 sa[2], pa[2];
+      bf16x8 pb[2][2], sb[2][2];
+      const f32x16 zero = {};
+      // dP starts from -delta of its rows, so the accumulator ends at
+      // dP - delta (the factor of dS besides P)
+      f32x16 nd0[2];
+  #pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 d4 =
+              *reinterpret_cast<const f32x4*>(Dt + mb * 32 + 16 * g + 4 * q4);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) nd0[mb][4 * q4 + e] = d4[e];
+        }
+      auto mfma = [&](auto i_c, const bf16x8& a) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < 2 * NA) {
+          constexpr int mb = i / NA, ks = (i % NA) / 2;
+          if constexpr (i % 2 == 0)
+            sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, kf[ks], ks == 0 ? zero : sa[mb], 0, 0, 0);
+          else
+            pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, vf[ks], ks == 0 ? nd0[mb] : pa[mb], 0, 0, 0);
+        } else {
+          constexpr int x = i - 2 * NA;
+          constexpr int mb = x / NB, r = x % NB;
+          constexpr int m2 = r / (2 * C::DB), db = (r % (2 * C::DB)) / 2;
+          if constexpr (r % 2 == 0)
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mb][m2],
+                                                              dva[db], 0, 0, 0);
+          else
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[mb][m2],
+                                                              dka[db], 0, 0, 0);
+        }
+      };
+
+      // softmax of rows 32 mb + 16 g + r of this tile (lane = key): a row
+      // outside [rlo, rhi) is masked unless the tile is full
+      const int r0 = t * kRT;
+      float pvv[16], dsv[16];
+      f32x4 l4;
+      int mlo[2], mhi[2];
+  #pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int base = r0 + mb * 32 + 16 * g;
+        mlo[mb] = rlo - base;
+        mhi[mb] = rhi - base;
       }
+      auto element = [&](auto mb_c, auto r_c) {
+        constexpr int mb = decltype(mb_c)::value, r = decltype(r_c)::value;
+        if constexpr (r % 4 == 0)
+          l4 = *reinterpret_cast<const f32x4*>(Lt + mb * 32 + 16 * g + r);
+        float pr = __builtin_amdgcn_exp2f(fmaf(sa[mb][r], cc, -l4[r % 4]));
+        if constexpr (!FULL) pr = (r >= mlo[mb] && r < mhi[mb]) ? pr : 0.f;
+        pvv[r] = pr;
+        dsv[r] = pr * pa[mb][r];
+        if constexpr (r % 8 == 7) {
+          constexpr int m2 = r / 8;
+          f32x8 x, y;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = pvv[8 * m2 + e];
+            y[e] = dsv[8 * m2 + e];
+          }
+          pb[mb][m2] = __builtin_convertvector(x, bf16x8);
+          sb[mb][m2] = __builtin_convertvector(y, bf16x8);
+        }
+      };
+
+      bf16x8 ring[RING];
+      static_for<0, AHEAD>([&](auto i_c) {
+        ring[decltype(i_c)::value] = fetch(i_c);
+      });
+      static_for<0, NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i + AHEAD < NM)
+          ring[(i + AHEAD) % RING] = fetch(ic<i + AHEAD>());
+        mfma(i_c, ring[i % RING]);
+        // softmax of rows 0 .. 31 during slots [NA, 2NA), of rows 32 .. 63
+        // during [2NA, 2NA+NB)
+        if constexpr (i >= NA && i < 2 * NA + NB) {
+          constexpr int mbs = (i < 2 * NA) ? 0 : 1;
+          constexpr int k = (i < 2 * NA) ? i - NA : i - 2 * NA;
+          static_for<0, EPS>([&](auto e_c) {
+            element(ic<mbs>(), ic<k * EPS + decltype(e_c)::value>());
+          });
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+      });
+    };
+    auto compute = [&](auto slot_c, int u) {
+      const int t = t_last - u / p.G;
+      if (!wave_needs(t)) return;
+      if (tile_full(t))
+        compute_t(slot_c, std::true_type(), t);
+      else
+        compute_t(slot_c, std::false_type(), t);
     };
 
-    bf16x8 ring[RING];
-    static_for<0, AHEAD>([&](auto i_c) {
-      ring[decltype(i_c)::value] = fetch(i_c);
-    });
-    static_for<0, NM>([&](auto i_c) {
-      constexpr int i = decltype(i_c)::value;
-      if constexpr (i + AHEAD < NM)
-        ring[(i + AHEAD) % RING] = fetch(ic<i + AHEAD>());
-      mfma(i_c, ring[i % RING]);
-      // softmax of rows 0 .. 31 during slots [NA, 2NA), of rows 32 .. 63
-      // during [2NA, 2NA+NB)
-      if constexpr (i >= NA && i < 2 * NA + NB) {
-        constexpr int mbs = (i < 2 * NA) ? 0 : 1;
-        constexpr int k = (i < 2 * NA) ? i - NA : i - 2 * NA;
-        static_for<0, EPS>([&](auto e_c) {
-          element(ic<mbs>(), ic<k * EPS + decltype(e_c)::value>());
+
+    // step u computes from slot u % 3 while the loads of step u + 2 fill slot
+    // (u + 2) % 3; before the barrier that ends step u each wave waits for its
+    // loads of step u + 1 (all but the nl loads it issued for step u + 2)
+    const int nl = (NL - wave + NW - 1) / NW;  // loads per step of this wave
+    if (nsteps > 0) {
+      issue(ic<0>(), 0);
+      if (1 < nsteps) {
+        issue(ic<1>(), 1);
+        wait_vmcnt_rt(nl);
+      } else {
+        wait_vm0();
+      }
+      barrier_nofence();
+      auto step = [&](auto slot_c, int u) {
+        constexpr int S = decltype(slot_c)::value;
+        const bool more = u + 2 < nsteps;
+        if (more) issue(ic<(S + 2) % 3>(), u + 2);
+        compute(slot_c, u);
+        if (more)
+          wait_vmcnt_rt(nl);
+        else
+          wait_vm0();
+        barrier_nofence();
+      };
+      for (int u = 0; u < nsteps; u += 3) {
+        step(ic<0>(), u);
+        if (u + 1 < nsteps) step(ic<1>(), u + 1);
+        if (u + 2 < nsteps) step(ic<2>(), u + 2);
+      }
+    }
+  } else {
+    // The work of a step is cut into two halves of 32 tile rows; half
+    // H = 2u + m is rows 32m .. 32m+31 of step u's tile (slot u % 3).  Each
+    // half passes through three stages:
+    //   SdP(H)   S = Q K^T and dP = dO V^T - delta (NA MFMAs, A = row-wise
+    //            LDS reads of Q / dO); on a tile that needs the mask, S starts
+    //            from -inf at the pairs the mask excludes (else from 0)
+    //   sm(H)    P = exp2(S c - lse2) and dS = P (dP - delta) in registers
+    //            (16 elements per lane), rounded to bf16; a masked pair has
+    //            S = -inf and c > 0, so its P is exactly 0
+    //   dKV(H)   dV^T += dO^T P and dK^T += Q^T dS (NB MFMAs, A = transposing
+    //            LDS reads of dO / Q)
+    // and the kernel runs them as a pipeline: phase H issues SdP(H+1), sm(H)
+    // and dKV(H-1), three independent streams, so the exponentials are spread
+    // over all the MFMAs and no phase waits on a result of its own.  Phase 2u
+    // reads slots u and u-1, phase 2u+1 slots u+1 and u; the workgroup
+    // barrier of step u sits between them (see below).  Each MFMA's A operand
+    // is read from LDS AHEAD MFMAs before it.
+    constexpr int NA = 2 * C::KS;   // SdP MFMAs of a half
+    constexpr int NB = 4 * C::DB;   // dKV MFMAs of a half
+    static_assert(NA == NB, "phase slots");
+    constexpr int AHEAD = 4;
+    constexpr int RING = AHEAD + 1;
+
+    f32x16 sa[2], pa[2];        // S and dP - delta of the last halves, by m
+    bf16x8 pb[2][2], sb[2][2];  // P and dS (bf16) of the last halves, by m
+    const f32x16 zero = {};
+  #pragma unroll
+    for (int m = 0; m < 2; ++m)
+  #pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        pb[m][m2] = bf16x8{};
+        sb[m][m2] = bf16x8{};
+      }
+
+    // One phase.  SN/MN: slot and m of the SdP half (tile tn); SC/MC: of the
+    // softmax half; SP/MP: of the dKV half.  DO_SDP / DO_SM / DO_KV switch the
+    // three streams (pipeline fill and drain).
+    auto phase = [&](auto sn_c, auto mn_c, auto sc_c, auto mc_c, auto sp_c,
+                     auto mp_c, auto do_sdp_c, auto do_sm_c, auto do_kv_c,
+                     int tn) __attribute__((always_inline)) {
+      constexpr int MN = decltype(mn_c)::value, MC = decltype(mc_c)::value;
+      constexpr int MP = decltype(mp_c)::value;
+      constexpr bool DO_SDP = decltype(do_sdp_c)::value;
+      constexpr bool DO_SM = decltype(do_sm_c)::value;
+      constexpr bool DO_KV = decltype(do_kv_c)::value;
+      const uint16_t* Qn = qslot(sn_c);
+      const uint16_t* On = oslot(sn_c);
+      const float* Dn = dslot(sn_c);
+      const float* Lc = lslot(sc_c);
+      const uint16_t* Qp = qslot(sp_c);
+      const uint16_t* Op = oslot(sp_c);
+
+      // the MFMAs of the phase in issue order: with both streams on, even
+      // slots are SdP and odd ones dKV
+      constexpr int NS = (DO_SDP ? NA : 0) + (DO_KV ? NB : 0);
+      constexpr bool BOTH = DO_SDP && DO_KV;
+      auto fetch = [&](auto i_c) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int k = BOTH ? i / 2 : i;
+        if constexpr (BOTH ? (i % 2 == 0) : DO_SDP) {
+          constexpr int ks = k / 2;
+          const uint16_t* tb = (k % 2 == 0) ? Qn : On;
+          return *reinterpret_cast<const bf16x8*>(tb + aoff[MN][ks]);
+        } else {
+          constexpr int m2 = k / (2 * C::DB), db = (k % (2 * C::DB)) / 2;
+          const uint16_t* tb = (k % 2 == 0) ? Op : Qp;
+          constexpr int c0 = (32 * MP + 8 * m2) * D;
+          return tr_pair(tb + toff[0][db] + c0, tb + toff[1][db] + c0 + 4 * D);
+        }
+      };
+      // S of the SdP half starts from its mask (0 or -inf), dP from -delta of
+      // its rows, so that the accumulator ends at dP - delta
+      f32x16 s0 = zero, nd0;
+      if constexpr (DO_SDP) {
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 d4 =
+              *reinterpret_cast<const f32x4*>(Dn + MN * 32 + 16 * g + 4 * q4);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) nd0[4 * q4 + e] = d4[e];
+        }
+        if (!tile_full(tn)) {
+          // rows 32 MN + 16 g + r of tile tn, allowed in [rlo, rhi)
+          const int base = tn * kRT + MN * 32 + 16 * g;
+          const int mlo = rlo - base, mhi = rhi - base;
+  #pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s0[r] = (r >= mlo && r < mhi) ? 0.f : -INFINITY;
+        }
+      }
+      auto mfma = [&](auto i_c, const bf16x8& a) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int k = BOTH ? i / 2 : i;
+        if constexpr (BOTH ? (i % 2 == 0) : DO_SDP) {
+          constexpr int ks = k / 2;
+          if constexpr (k % 2 == 0)
+            sa[MN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, kf[ks], ks == 0 ? s0 : sa[MN], 0, 0, 0);
+          else
+            pa[MN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, vf[ks], ks == 0 ? nd0 : pa[MN], 0, 0, 0);
+        } else {
+          constexpr int m2 = k / (2 * C::DB), db = (k % (2 * C::DB)) / 2;
+          if constexpr (k % 2 == 0)
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[MP][m2],
+                                                              dva[db], 0, 0, 0);
+          else
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[MP][m2],
+                                                              dka[db], 0, 0, 0);
+        }
+      };
+
+      // softmax of rows 32 MC + 16 g + r of the softmax half (lane = key)
+      float pvv[16], dsv[16];
+      f32x4 l4;
+      auto element = [&](auto r_c) __attribute__((always_inline)) {
+        constexpr int r = decltype(r_c)::value;
+        if constexpr (r % 4 == 0)
+          l4 = *reinterpret_cast<const f32x4*>(Lc + MC * 32 + 16 * g + r);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sa[MC][r], cc, -l4[r % 4]));
+        pvv[r] = pr;
+        dsv[r] = pr * pa[MC][r];
+        if constexpr (r % 8 == 7) {
+          constexpr int m2 = r / 8;
+          f32x8 x, y;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = pvv[8 * m2 + e];
+            y[e] = dsv[8 * m2 + e];
+          }
+          pb[MC][m2] = __builtin_convertvector(x, bf16x8);
+          sb[MC][m2] = __builtin_convertvector(y, bf16x8);
+        }
+      };
+
+      if constexpr (NS > 0) {
+        bf16x8 ring[RING];
+        static_for<0, (AHEAD < NS ? AHEAD : NS)>(
+            [&](auto i_c) __attribute__((always_inline)) {
+              ring[decltype(i_c)::value] = fetch(i_c);
+            });
+        static_for<0, NS>([&](auto i_c) __attribute__((always_inline)) {
+          constexpr int i = decltype(i_c)::value;
+          if constexpr (i + AHEAD < NS)
+            ring[(i + AHEAD) % RING] = fetch(ic<i + AHEAD>());
+          mfma(i_c, ring[i % RING]);
+          // the softmax's 16 elements spread over the phase's MFMAs
+          if constexpr (DO_SM) {
+            static_for<i * 16 / NS, (i + 1) * 16 / NS>(
+                [&](auto e_c) __attribute__((always_inline)) {
+                  element(e_c);
+                });
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        });
+      } else if constexpr (DO_SM) {
+        static_for<0, 16>([&](auto e_c) __attribute__((always_inline)) {
+          element(e_c);
         });
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-    });
-  };
-  auto compute = [&](auto slot_c, int u) {
-    const int t = t_last - u / p.G;
-    if (!wave_needs(t)) return;
-    if (tile_full(t))
-      compute_t(slot_c, std::true_type(), t);
-    else
-      compute_t(slot_c, std::false_type(), t);
-  };
-
-
-  // step u computes from slot u % 3 while the loads of step u + 2 fill slot
-  // (u + 2) % 3; before the barrier that ends step u each wave waits for its
-  // loads of step u + 1 (all but the nl loads it issued for step u + 2)
-  const int nl = (NL - wave + NW - 1) / NW;  // loads per step of this wave
-  if (nsteps > 0) {
-    issue(ic<0>(), 0);
-    if (1 < nsteps) {
-      issue(ic<1>(), 1);
-      wait_vmcnt_rt(nl);
-    } else {
-      wait_vm0();
-    }
-    barrier_nofence();
-    auto step = [&](auto slot_c, int u) {
-      constexpr int S = decltype(slot_c)::value;
-      const bool more = u + 2 < nsteps;
-      if (more) issue(ic<(S + 2) % 3>(), u + 2);
-      compute(slot_c, u);
-      if (more)
-        wait_vmcnt_rt(nl);
-      else
-        wait_vm0();
-      barrier_nofence();
     };
-    for (int u = 0; u < nsteps; u += 3) {
-      step(ic<0>(), u);
-      if (u + 1 < nsteps) step(ic<1>(), u + 1);
-      if (u + 2 < nsteps) step(ic<2>(), u + 2);
+
+    using T = std::true_type;
+    using F = std::false_type;
+    auto tile_of_step = [&](int u) { return t_last - u / p.G; };
+    // Step u (slot S = u % 3): phase 2u, then each wave waits for its loads of
+    // step u + 1 and takes the barrier, then issues the loads of step u + 2
+    // into slot (u + 2) % 3 (last read in phase 2u, by dKV(2u - 1)), then
+    // phase 2u + 1.  Before step 0: the loads of steps 0 and 1, slot 2's tiles
+    // zeroed (phase 0's dKV(-1) reads them, with zero P and dS), the barrier,
+    // and SdP(0).  After the last step n - 1: dKV(2n - 1).  Phase 2n - 1 also
+    // forms SdP(2n) from a stale slot; that result is never used.
+    if (nsteps > 0) {
+      issue(ic<0>(), 0);
+      if (1 < nsteps) issue(ic<1>(), 1);
+      {
+        constexpr int CHUNKS = C::TILE / 8;  // 16-byte chunks per tile
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int c = tid; c < CHUNKS; c += 64 * NW) {
+          *reinterpret_cast<u32x4*>(Qs2 + 8 * c) = z;
+          *reinterpret_cast<u32x4*>(Os2 + 8 * c) = z;
+        }
+      }
+      wait_vm0();
+      __syncthreads();
+      phase(ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), T(), F(), F(),
+            tile_of_step(0));
+      auto step = [&](auto s_c, int u) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        constexpr int S1 = (S + 1) % 3, S2 = (S + 2) % 3;
+        phase(ic<S>(), ic<1>(), ic<S>(), ic<0>(), ic<S2>(), ic<1>(), T(), T(),
+              T(), tile_of_step(u));
+        wait_vm0();
+        barrier_nofence();
+        if (u + 2 < nsteps) issue(ic<S2>(), u + 2);
+        phase(ic<S1>(), ic<0>(), ic<S>(), ic<1>(), ic<S>(), ic<0>(), T(), T(),
+              T(), tile_of_step(u + 1));
+      };
+      int u = 0;
+      for (; u + 3 <= nsteps; u += 3) {
+        step(ic<0>(), u);
+        step(ic<1>(), u + 1);
+        step(ic<2>(), u + 2);
+      }
+      if (u < nsteps) step(ic<0>(), u++);
+      if (u < nsteps) step(ic<1>(), u++);
+      // dKV(2n - 1): slot (n - 1) % 3
+      const int sl = (nsteps - 1) % 3;
+      if (sl == 0)
+        phase(ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<1>(), F(), F(), T(),
+              0);
+      else if (sl == 1)
+        phase(ic<1>(), ic<0>(), ic<1>(), ic<0>(), ic<1>(), ic<1>(), F(), F(), T(),
+              0);
+      else
+        phase(ic<2>(), ic<0>(), ic<2>(), ic<0>(), ic<2>(), ic<1>(), F(), F(), T(),
+              0);
     }
   }
 
@@ -888,7 +1130,7 @@ hipError_t launch_all(BwdParams p, hipStream_t st) {
   BwdParams a = p;
   a.nblk = (p.Nk + kWR * NWK - 1) / (kWR * NWK);
   a.total = p.B * p.Hkv * a.nblk;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK>), dim3(a.total),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK, D == 128>), dim3(a.total),
                      dim3(64 * NWK), 0, st, a);
   BwdParams c = p;
   c.nblk = (p.Nq + kWR * NWQ - 1) / (kWR * NWQ);
