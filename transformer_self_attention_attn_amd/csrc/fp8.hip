@@ -570,7 +570,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
         u = __builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], u, true);
         wb[mb * 4 + r / 4] = (int)u;
       }
-    l += ls * (1.0f / vr);
+    l += ls * __builtin_amdgcn_rcpf(vr);  // 1 ulp; vr in [2^-100, 1]
   };
 
   // O^T += V^T W^T over tile t's keys
