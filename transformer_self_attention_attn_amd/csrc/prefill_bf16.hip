@@ -464,14 +464,15 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   // SLK from resource krs, V into slot SLV from vrs); the weights of tile t
   // stay in
   // `sc` (fp32) for Y(t).
-  auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, miattn_i32x4 krs,
-                   miattn_i32x4 vrs, int t,
+  auto tileX = [&](auto sk_c, auto slk_c, auto slv_c, auto full_c,
+                   miattn_i32x4 krs, miattn_i32x4 vrs, int t,
                    f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int SK = decltype(sk_c)::value;
+    constexpr bool FULL = decltype(full_c)::value != 0;
     const int j0 = t * kKT;
     float mx = mx_pre;
     // lane holds keys j0 + mb*32 + g*16 + r (r = 0..15) of query qi
-    if (!tile_full(t)) {
+    if (!FULL && !tile_full(t)) {
       // this lane's keys of block mb are jb + r, r = 0 .. 15; the bounds are
       // taken relative to jb so that each test compares with a constant r
       if (p.window == 0 && p.sinks == 0) {  // keys below hw only
@@ -673,8 +674,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     if (!il && ld_v) dma_v(ic<SLV>(), rv);
     if (!il && ld_k) dma_k(ic<SLK>(), rk);
     if (il) {
-      tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), tile_rsrc(kg, rk, ld_k),
-            tile_rsrc(vg, rv, ld_v), rt, sc, sn);
+      tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), ic<0>(),
+            tile_rsrc(kg, rk, ld_k), tile_rsrc(vg, rv, ld_v), rt, sc, sn);
     } else if (t + 1 < nt && wave_needs(tile_of(t + 1))) {
       qk(ic<(K + 1) % 2>(), sn);
       mx_pre = -INFINITY;
@@ -687,13 +688,66 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     wait_vmcnt(0);
     barrier_nofence();
   };
+  // Interior steps [la, lb) of the longer run (the window run when there are
+  // two): the wave needs all of the tile with no mask, and the K and V tiles
+  // loaded in the step belong to the same run and lie wholly below the valid
+  // length.  Such a step is the one above with every decision known: the
+  // step works on tile t + toff, its loads read whole 64-row tiles, and no
+  // tile bounds are evaluated.  The sink clause of tile_full is left out
+  // (fewer lean steps, never a wrong one).
+  int la = 0, lb = 0;
+  const int s0 = nt > nA ? nA : 0, s1 = nt > nA ? nt : nA;
+  const int toff = nt > nA ? tB0 - nA : 0;
+  if (wlive) {
+    const int f0 = (w_lo_max + kKT - 1) / kKT;  // first tile with no key left of a row's window
+    const int f1 = w_hi_min / kKT;              // tiles below: no key right of it
+    la = max(s0, f0 - toff);
+    lb = min(min(s1 - 2, f1 - toff), L / kKT - 2 - toff);
+  }
+  const miattn_i32x4 krs0 = dev::rows_rsrc(kg + (size_t)toff * kKT * D, kKT * D * 2);
+  const miattn_i32x4 vrs0 = dev::rows_rsrc(vg + (size_t)toff * kKT * D, kKT * D * 2);
+  // resource of whole tile t + toff, from the run's base: the 64-bit base
+  // advances by whole tiles
+  auto lean_rsrc = [&](miattn_i32x4 r0, int t) {
+    const unsigned long long a =
+        ((unsigned long long)(unsigned)r0[1] << 32 | (unsigned)r0[0]) +
+        (unsigned long long)(unsigned)t * (kKT * D * 2);
+    miattn_i32x4 r = r0;
+    r[0] = (int)(unsigned)a;
+    r[1] = (int)((unsigned)(a >> 32) & 0xffffu);
+    return r;
+  };
+  auto lean = [&](auto k_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int K = decltype(k_c)::value;
+    constexpr int SLK = K % 2, SLV = (K + 1) % 2;
+    tileX(ic<(K + 1) % 2>(), ic<SLK>(), ic<SLV>(), ic<1>(),
+          lean_rsrc(krs0, t + 2), lean_rsrc(vrs0, t + 1), t + toff, sc, sn);
+    tileY(ic<K % 2>(), sc, sn);
+    wait_vmcnt(0);
+    barrier_nofence();
+  };
   // Unrolled by 2: every ring slot index is a compile-time constant and the
   // two score buffers swap roles without copies (the loop leaves from inside
   // the pair: the buffers are dead after it, so no join needs a copy).
-  for (int t = 0; t < nt; t += 2) {
+  // The lean pairs start at the first even step from la on.
+  const int lp0 = la + (la & 1);
+  const int lp1 = lp0 + 1 < lb ? lp0 + ((lb - lp0) & ~1) : lp0;  // end of the pairs
+  int t = 0;
+  for (; t < (lp1 > lp0 ? lp0 : nt); t += 2) {
     step(ic<0>(), t, sa, sb);
     if (t + 1 >= nt) break;
     step(ic<1>(), t + 1, sb, sa);
+  }
+  if (lp1 > lp0) {
+    for (; t < lp1; t += 2) {
+      lean(ic<0>(), t, sa, sb);
+      lean(ic<1>(), t + 1, sb, sa);
+    }
+    for (; t < nt; t += 2) {
+      step(ic<0>(), t, sa, sb);
+      if (t + 1 >= nt) break;
+      step(ic<1>(), t + 1, sb, sa);
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------
