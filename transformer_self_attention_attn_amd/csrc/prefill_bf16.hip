@@ -565,7 +565,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
                C::VLOADS);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, EPS, 0);      // VALU
+      __builtin_amdgcn_sched_group_barrier(0x400, EPS, 0);      // exp
       if (i < C::KLW + C::VLW)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
     }
