@@ -336,7 +336,8 @@ def run_only(args):
     stream = torch.cuda.current_stream(dev)
     name = args.only
     bwd = name == "backward"
-    w = synth.by_name("gqa-causal-prefill" if bwd else name)
+    f8 = name == "fp8"
+    w = synth.by_name("gqa-causal-prefill" if bwd or f8 else name)
     seed = args.seed if args.seed is not None else SEEDS.get(w.name, 0)
     x = synth.make_inputs(w, seed)
     sl = None if x["seqlens"] is None else \
@@ -364,6 +365,14 @@ def run_only(args):
                              w.sinks, 0 if sl is None else sl.data_ptr(),
                              stream.cuda_stream)
             assert rc == mi.MIATTN_OK, mi.attn_last_error()
+    if f8:
+        # quantize (block scales, Q and K rotated), then the forward on the
+        # codes: one launch of each kernel per rep
+        sg = torch.from_numpy(synth.make_signs(w.d, seed)).to(dev)
+
+        def fn(i):
+            z = mi.fp8_quantize(q, k, v, seqlens=sl, signs=sg)
+            mi.attn_fp8(z, causal=w.causal, seqlens=sl, out=o, lse=lse)
     for i in range(args.warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -378,7 +387,7 @@ def run_only(args):
     torch.cuda.synchronize()
     prot = trimmed([a.elapsed_time(b) for a, b in ev])
     rec = {"only": name, "seed": seed, "shape": shape_str(w), **prot}
-    if not bwd and not decode_shaped(w):
+    if not bwd and not f8 and not decode_shaped(w):
         rec["roofline"] = prefill_roofline(w, x["seqlens"],
                                            prot["trimmed_mean_ms"] * 1e-3)
     print(json.dumps(rec), flush=True)
@@ -405,7 +414,9 @@ def main():
                     help="time the step only (no other configurations, "
                          "backward, FP8, chunks or local windows)")
     ap.add_argument("--only", metavar="WORKLOAD",
-                    help="run one workload (or `backward`) alone and exit")
+                    help="run one workload (or `backward`, or `fp8`: the FP8 "
+                         "quantizer and forward on gqa-causal-prefill) alone "
+                         "and exit")
     ap.add_argument("--seed", type=int, default=None,
                     help="input seed for --only (default: the workload's)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
