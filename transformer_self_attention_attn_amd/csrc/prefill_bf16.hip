@@ -71,6 +71,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "fastdiv.h"
 
 // Workgroup shape per head dimension, chosen by measurement on MI355X: both
 // run 4 wavefronts (128 query rows share each K/V tile) with at least two
@@ -178,6 +179,16 @@ __device__ inline float half_swap_max(float x) {
   return a;
 }
 
+// x of this lane plus x of the lane 32 away, the same way
+__device__ inline float half_swap_add(float x) {
+  float a = x, b = x;
+  asm volatile(
+      "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_add_f32 %0, %0, %1"
+      : "+v"(a), "+v"(b));
+  return a;
+}
+
 struct PrefillParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -189,6 +200,10 @@ struct PrefillParams {
   int qband;       // query blocks per band of the causal block order
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
+  // the block order's divisors: blocks of a band across the XCD's groups
+  // (groups per XCD x qband x G), of one group's band (qband x G), G, Hkv,
+  // and the blocks of one group (G x nqb)
+  UDiv dv_band, dv_bs, dv_g, dv_hkv, dv_grp;
 };
 
 template <int I>
@@ -227,34 +242,36 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   // by band (qband query blocks each, enough blocks to fill the XCD's
   // slots), one group at a time within a band, so that the XCD's L2 mostly
   // holds one group's K/V.
+  // (the divisions by launch-fixed values go through fastdiv.h)
   const int n = p.total;
   const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int slot = bid / kXcds;
+  const int xcd = (int)((unsigned)bid % kXcds);
+  const int slot = (int)((unsigned)bid / kXcds);
   const int ngrp = p.B * p.Hkv;
   int grp, qrank, hh;
   if (p.causal && ngrp % kXcds == 0) {
-    const int gpx = ngrp / kXcds;  // groups per XCD
+    const int gpx = (int)((unsigned)ngrp / kXcds);  // groups per XCD
     const int bs = p.qband * p.G;  // blocks of one group in a band
-    const int band = slot / (gpx * bs);
+    const int band = udiv(slot, p.dv_band);
     const int r1 = slot - band * gpx * bs;
-    const int gi = r1 / bs;
+    const int gi = udiv(r1, p.dv_bs);
     const int r2 = r1 - gi * bs;
-    qrank = band * p.qband + r2 / p.G;
+    const int r2g = udiv(r2, p.dv_g);
+    qrank = band * p.qband + r2g;
     grp = xcd * gpx + gi;
-    hh = r2 - (r2 / p.G) * p.G;
+    hh = r2 - r2g * p.G;
   } else {
-    const int per = n / kXcds;
-    const int rem = n % kXcds;
+    const int per = (int)((unsigned)n / kXcds);
+    const int rem = (int)((unsigned)n % kXcds);
     const int lid = xcd * per + min(xcd, rem) + slot;
     const int per_grp = p.G * p.nqb;
-    grp = lid / per_grp;
+    grp = udiv(lid, p.dv_grp);
     const int r0 = lid - grp * per_grp;
-    qrank = r0 / p.G;
+    qrank = udiv(r0, p.dv_g);
     hh = r0 - qrank * p.G;
   }
   const int qb = p.causal ? (p.nqb - 1 - qrank) : qrank;
-  const int b = grp / p.Hkv;
+  const int b = udiv(grp, p.dv_hkv);
   const int hk = grp - b * p.Hkv;
   const int h = hk * p.G + hh;
 
@@ -360,9 +377,16 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     if (qlive) {
       raw = *reinterpret_cast<const u32x4*>(p.q + qo_base + (size_t)qi * D +
                                             16 * ks + 8 * g);
-      raw ^= p.qsign;
     }
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+  if (p.qsign != 0) {  // negative scale: Q negated (uniform branch)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 raw = __builtin_bit_cast(u32x4, qf[ks]);
+      raw ^= p.qsign;
+      qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
   }
 
   // ---- direct-to-LDS tile loads ---------------------------------------------
@@ -752,10 +776,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   }
 
   // ---- epilogue -----------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = half_swap_add(l);
   if (qi < p.Nq) {
     const bool any = qlive && lt > 0.f;
-    const float inv = any ? 1.f / lt : 0.f;
+    const float inv = any ? __builtin_amdgcn_rcpf(lt) : 0.f;  // 1 ulp
     uint16_t* orow = p.o + qo_base + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -794,6 +818,12 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
         if (qb * p.G >= slots) break;
       }
   }
+  const int gpx = p.B * p.Hkv / kXcds;
+  p.dv_band = make_udiv(gpx * p.qband * p.G);
+  p.dv_bs = make_udiv(p.qband * p.G);
+  p.dv_g = make_udiv(p.G);
+  p.dv_hkv = make_udiv(p.Hkv);
+  p.dv_grp = make_udiv(p.G * p.nqb);
   hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
 }
