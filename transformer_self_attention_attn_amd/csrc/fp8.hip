@@ -50,6 +50,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "block_order.h"
 #include "device_common.h"
 
 namespace miattn {
@@ -299,6 +300,7 @@ struct Fp8Params {
   int causal, window, window_right, sinks;
   float c;  // |scale| * log2(e) (divided by d for rotated operands)
   unsigned qsign;  // 0x80808080 when the scale is negative: Q codes negated
+  BlockOrder order;  // block -> (batch, head, query block): block_order.h
 };
 
 template <int D, int NW>
@@ -321,17 +323,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
     if constexpr (decltype(s)::value == 0) return Vs0; else return Vs1;
   };
 
-  // block -> (batch, K/V head, query block, head of the group), blocks of a
-  // group on one XCD; causal blocks heaviest first
-  const int lid = xcd_block(blockIdx.x, p.total);
-  const int per_grp = p.G * p.nqb;
-  const int grp = lid / per_grp;
-  const int r0g = lid - grp * per_grp;
-  const int qrank = r0g / p.G;
-  const int hh = r0g - qrank * p.G;
-  const int qb = p.causal ? (p.nqb - 1 - qrank) : qrank;
-  const int b = grp / p.Hkv;
-  const int hk = grp - b * p.Hkv;
+  // block -> (batch, K/V head, query block, head of the group): the order
+  // of block_order.h (whole groups per XCD, causal blocks heaviest first)
+  const BlockPos bpos = block_pos(blockIdx.x, p.order);
+  const int qb = bpos.qb;
+  const int b = bpos.b;
+  const int hk = bpos.hk;
+  const int hh = bpos.hh;
   const int h = hk * p.G + hh;
   const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
 
@@ -783,6 +781,9 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
   static_assert(NW == lanes::kFp8Waves, "shared lane layout");
   p.nqb = (pr.Nq + kWR * NW - 1) / (kWR * NW);
   p.total = pr.B * pr.Hq * p.nqb;
+  // K and V^T codes of one group: 2 Nkp d bytes; two workgroups per CU
+  p.order = make_block_order(pr.B, pr.Hkv, p.G, p.nqb, pr.causal != 0,
+                             2LL * p.Nkp * pr.d, 32 * 2);
   if (pr.d == 128)
     hipLaunchKernelGGL((attn_fp8_kernel<128, NW>), dim3(p.total),
                        dim3(64 * NW), 0, stream, p);

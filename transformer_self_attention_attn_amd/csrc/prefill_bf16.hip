@@ -71,7 +71,7 @@
 #include <type_traits>
 
 #include "device_common.h"
-#include "fastdiv.h"
+#include "block_order.h"
 
 // Workgroup shape per head dimension, chosen by measurement on MI355X: both
 // run 4 wavefronts (128 query rows share each K/V tile) with at least two
@@ -99,7 +99,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kQW = 32;          // query rows per wavefront
 constexpr int kKT = 64;          // keys per tile
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
-constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies
 
 template <int D, int NW>
 struct Cfg {
@@ -197,13 +196,9 @@ struct PrefillParams {
   float* lse;
   const int* seqlens;
   int B, Hq, Hkv, Nq, Nk, G, nqb, causal, window, window_right, sinks, total;
-  int qband;       // query blocks per band of the causal block order
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
-  // the block order's divisors: blocks of a band across the XCD's groups
-  // (groups per XCD x qband x G), of one group's band (qband x G), G, Hkv,
-  // and the blocks of one group (G x nqb)
-  UDiv dv_band, dv_bs, dv_g, dv_hkv, dv_grp;
+  BlockOrder order;  // block -> (batch, head, query block): block_order.h
 };
 
 template <int I>
@@ -232,47 +227,13 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   };
 
   // ---- block -> (batch, head, query block) --------------------------------
-  // Blocks are dealt round-robin to the 8 XCDs (block id mod 8).  Each XCD
-  // gets whole (batch, K/V head) groups, so a group's K/V tiles meet in one
-  // L2.  Under the causal mask a query block's work grows with its index:
-  // when the groups divide evenly over the XCDs, each XCD runs its blocks
-  // heaviest first across all of its groups (longest job first), so that no
-  // long diagonal block starts late; otherwise heaviest first within each
-  // group.  Where a group's K/V is large, the heaviest-first order goes band
-  // by band (qband query blocks each, enough blocks to fill the XCD's
-  // slots), one group at a time within a band, so that the XCD's L2 mostly
-  // holds one group's K/V.
-  // (the divisions by launch-fixed values go through fastdiv.h)
-  const int n = p.total;
-  const int bid = blockIdx.x;
-  const int xcd = (int)((unsigned)bid % kXcds);
-  const int slot = (int)((unsigned)bid / kXcds);
-  const int ngrp = p.B * p.Hkv;
-  int grp, qrank, hh;
-  if (p.causal && ngrp % kXcds == 0) {
-    const int gpx = (int)((unsigned)ngrp / kXcds);  // groups per XCD
-    const int bs = p.qband * p.G;  // blocks of one group in a band
-    const int band = udiv(slot, p.dv_band);
-    const int r1 = slot - band * gpx * bs;
-    const int gi = udiv(r1, p.dv_bs);
-    const int r2 = r1 - gi * bs;
-    const int r2g = udiv(r2, p.dv_g);
-    qrank = band * p.qband + r2g;
-    grp = xcd * gpx + gi;
-    hh = r2 - r2g * p.G;
-  } else {
-    const int per = (int)((unsigned)n / kXcds);
-    const int rem = (int)((unsigned)n % kXcds);
-    const int lid = xcd * per + min(xcd, rem) + slot;
-    const int per_grp = p.G * p.nqb;
-    grp = udiv(lid, p.dv_grp);
-    const int r0 = lid - grp * per_grp;
-    qrank = udiv(r0, p.dv_g);
-    hh = r0 - qrank * p.G;
-  }
-  const int qb = p.causal ? (p.nqb - 1 - qrank) : qrank;
-  const int b = udiv(grp, p.dv_hkv);
-  const int hk = grp - b * p.Hkv;
+  // the order of block_order.h: whole (batch, K/V head) groups per XCD,
+  // causal blocks heaviest first
+  const BlockPos bpos = block_pos(blockIdx.x, p.order);
+  const int qb = bpos.qb;
+  const int b = bpos.b;
+  const int hk = bpos.hk;
+  const int hh = bpos.hh;
   const int h = hk * p.G + hh;
 
   int L = p.Nk;
@@ -809,21 +770,8 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
   // the smallest divisor of nqb whose band of one group (qband * G blocks)
   // fills an XCD's workgroup slots (32 CUs); otherwise 1 (plain heaviest
   // first across the XCD's groups)
-  p.qband = 1;
-  if (2LL * p.Nk * D * 2 >= (1LL << 20)) {
-    const int slots = 32 * (D == 64 ? 3 : 2);
-    for (int qb = 1; qb <= p.nqb; ++qb)
-      if (p.nqb % qb == 0) {
-        p.qband = qb;
-        if (qb * p.G >= slots) break;
-      }
-  }
-  const int gpx = p.B * p.Hkv / kXcds;
-  p.dv_band = make_udiv(gpx * p.qband * p.G);
-  p.dv_bs = make_udiv(p.qband * p.G);
-  p.dv_g = make_udiv(p.G);
-  p.dv_hkv = make_udiv(p.Hkv);
-  p.dv_grp = make_udiv(p.G * p.nqb);
+  p.order = make_block_order(p.B, p.Hkv, p.G, p.nqb, p.causal != 0,
+                             2LL * p.Nk * D * 2, 32 * (D == 64 ? 3 : 2));
   hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
 }
