@@ -54,6 +54,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "block_order.h"
 #include "device_common.h"
 
 
@@ -92,6 +93,7 @@ struct BwdParams {
   int nblk, total;  // blocks per (batch, head) and in the grid
   float c;          // scale * log2(e)
   float scale;
+  BlockOrder order;  // dQ kernel: block -> (batch, head, query block)
 };
 
 template <int D>
@@ -844,17 +846,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     if constexpr (decltype(s)::value == 0) return Vs0; else return Vs1;
   };
 
-  // (batch, K/V head, query block, head of the group); causal blocks run
-  // heaviest (last rows) first
-  const int lid = xcd_block(blockIdx.x, p.total);
-  const int per_grp = p.G * p.nblk;
-  const int grp = lid / per_grp;
-  const int r0g = lid - grp * per_grp;
-  const int qrank = r0g / p.G;
-  const int hh = r0g - qrank * p.G;
-  const int qb = p.causal ? (p.nblk - 1 - qrank) : qrank;
-  const int b = grp / p.Hkv;
-  const int hk = grp - b * p.Hkv;
+  // (batch, K/V head, query block, head of the group): the order of
+  // block_order.h, as for the forward (whole groups per XCD, causal blocks
+  // heaviest first across an XCD's groups)
+  const BlockPos bpos = block_pos(blockIdx.x, p.order);
+  const int qb = bpos.qb;
+  const int b = bpos.b;
+  const int hk = bpos.hk;
+  const int hh = bpos.hh;
   const int h = hk * p.G + hh;
   const Seq s = seq_of(p.seqlens, p.Nq, p.Nk, b);
   auto row_keys = [&](bool live, int pos) {
@@ -1135,6 +1134,8 @@ hipError_t launch_all(BwdParams p, hipStream_t st) {
   BwdParams c = p;
   c.nblk = (p.Nq + kWR * NWQ - 1) / (kWR * NWQ);
   c.total = p.B * p.Hq * c.nblk;
+  c.order = make_block_order(p.B, p.Hkv, p.G, c.nblk, p.causal != 0,
+                             2LL * p.Nk * D * 2, 32 * 2);
   hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3(c.total), dim3(64 * NWQ),
                      0, st, c);
   return hipGetLastError();
