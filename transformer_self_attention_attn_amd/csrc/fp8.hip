@@ -461,26 +461,28 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
   const size_t kvh = (size_t)(b * p.Hkv + hk) * p.Nkp * D;
   const miattn_i32x4 krs = rows_rsrc(p.k8 + kvh, p.Nkp * D);
   const miattn_i32x4 vrs = rows_rsrc(p.v8t + kvh, p.Nkp * D);
+  // Wave w issues loads w + NW m: the K tile's KL loads split evenly over
+  // the waves, so a wave's first KL / NW loads are K and the rest V^T, the
+  // same m for every wave (no test per load)
+  constexpr int KL = KT / 1024;
+  static_assert(KL % NW == 0 && LOADS == LW * NW, "even split of the loads");
   auto issue_k = [&](auto slot_c, int u) {
     const unsigned tb = (unsigned)(tile_of(u) * KT);
 #pragma unroll
-    for (int m = 0; m < LW; ++m) {
+    for (int m = 0; m < KL / NW; ++m) {
       const int u2 = wave + NW * m;
-      if (u2 < KT / 1024)
-        miattn_buffer_load_lds(
-            krs, (lds_void*)(kslot(slot_c) + u2 * 1024), 16, toffs[m] + tb,
-            0, 0, 0);
+      miattn_buffer_load_lds(krs, (lds_void*)(kslot(slot_c) + u2 * 1024), 16,
+                             toffs[m] + tb, 0, 0, 0);
     }
   };
   auto issue_v = [&](auto slot_c, int u) {
     const unsigned tb = (unsigned)(tile_of(u) * KT);
 #pragma unroll
-    for (int m = 0; m < LW; ++m) {
+    for (int m = KL / NW; m < LW; ++m) {
       const int u2 = wave + NW * m;
-      if (u2 >= KT / 1024 && u2 < LOADS)
-        miattn_buffer_load_lds(
-            vrs, (lds_void*)(vslot(slot_c) + (u2 - KT / 1024) * 1024), 16,
-            toffs[m] + tb, 0, 0, 0);
+      miattn_buffer_load_lds(vrs,
+                             (lds_void*)(vslot(slot_c) + (u2 - KL) * 1024), 16,
+                             toffs[m] + tb, 0, 0, 0);
     }
   };
 
