@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "fastdiv.h"
 
 namespace miattn {
 namespace {
@@ -81,6 +82,8 @@ struct DecodeParams {
   int B, Hq, Hkv, Nq, Nk, G, ncols, nhc, causal, window, window_right, sinks,
       nsplit, chunk;
   float c;  // scale * log2(e)
+  // divisions by launch-fixed values (fastdiv.h): Hkv * nhc, nhc, Nq, chunk
+  UDiv dv_nx, dv_nhc, dv_nq, dv_chunk;
 };
 
 // Valid length of batch b.
@@ -134,12 +137,21 @@ __device__ inline float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
   return x;
 }
-__device__ inline int wave_min_i(int x) {
-  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m));
+// Minimum / maximum over the 16 lanes of each row (lanes 16r .. 16r+15),
+// left in every lane of the row: rotations of the row by 8, 4, 2 and 1
+// through DPP, with no LDS round trip.
+__device__ inline int row_min_i(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false));
   return x;
 }
-__device__ inline int wave_max_i(int x) {
-  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m));
+__device__ inline int row_max_i(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false));
   return x;
 }
 
@@ -285,8 +297,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   // XCD sees every split index equally often, whatever the valid lengths.
   const int s = blockIdx.y;
   const int nx = p.Hkv * p.nhc;
-  const int b = blockIdx.x / nx;
-  const int hk = (blockIdx.x - b * nx) / p.nhc;
+  const int b = udiv(blockIdx.x, p.dv_nx);
+  const int hk = udiv(blockIdx.x - b * nx, p.dv_nhc);
   const int hc = blockIdx.x - b * nx - hk * p.nhc;
   const int lane = threadIdx.x;
   const int n = lane & 15;   // MFMA column (S^T, O^T), key row (K)
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   // column n of this block: query head hk*G + cl / Nq, row cl % Nq
   const int cl = hc * 16 + n;
   const bool cvalid = cl < p.ncols;
-  const int hh = cvalid ? cl / p.Nq : 0;
+  const int hh = cvalid ? udiv(cl, p.dv_nq) : 0;
   const int row = cvalid ? cl - hh * p.Nq : 0;
   const size_t qrow = ((size_t)(b * p.Hq + hk * p.G + hh)) * p.Nq + row;
 
@@ -317,8 +329,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   // from a0 to c1 (the union over its columns)
   const int c0 = s * p.chunk;
   const int cend = c0 + p.chunk;
-  const int a0 = wave_min_i(split_first(rk, c0, cend));
-  const int c1 = wave_max_i(split_end(rk, c0, cend));
+  // (a lane's keys depend only on its column n, so the four rows of the
+  // wave hold the same 16 values and a row's extremum is the wave's)
+  const int a0 =
+      __builtin_amdgcn_readfirstlane(row_min_i(split_first(rk, c0, cend)));
+  const int c1 =
+      __builtin_amdgcn_readfirstlane(row_max_i(split_end(rk, c0, cend)));
   if (a0 >= c1) return;  // no allowed key here; the combine skips this split
   const int kt0 = c0 + (a0 - c0) / kKT * kKT;  // first key of the first tile
   const int nt = (c1 - kt0 + kKT - 1) / kKT;   // tiles of this split
@@ -474,7 +490,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
   if (r >= p.B * p.Hq * p.Nq) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int b = r / (p.Hq * p.Nq);
-  const int row = r - (r / p.Nq) * p.Nq;
+  const int row = r - udiv(r, p.dv_nq) * p.Nq;
   const int L = valid_len(p, b);
   const RowKeys rk = row_keys(p, L, row);
   const size_t row0 = (size_t)r * p.nsplit;
@@ -486,8 +502,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(
     return;
   }
   // the splits holding keys of this row (their blocks wrote them)
-  const int s0 = rk.sk > 0 ? 0 : rk.lo / p.chunk;
-  const int s1 = (max(rk.hw, rk.sk) + p.chunk - 1) / p.chunk;
+  const int s0 = rk.sk > 0 ? 0 : udiv(rk.lo, p.dv_chunk);
+  const int s1 = udiv(max(rk.hw, rk.sk) + p.chunk - 1, p.dv_chunk);
   auto live = [&](int s) {
     const int c0 = s * p.chunk;
     return split_first(rk, c0, c0 + p.chunk) < c0 + p.chunk;
@@ -579,6 +595,10 @@ hipError_t launch_decode_bf16(const void* q, const void* k, const void* v,
   p.chunk = decode_chunk(pr);
   p.nsplit = (pr.Nk + p.chunk - 1) / p.chunk;
   p.c = pr.scale * 1.4426950408889634f;
+  p.dv_nx = make_udiv(p.Hkv * p.nhc);
+  p.dv_nhc = make_udiv(p.nhc);
+  p.dv_nq = make_udiv(p.Nq);
+  p.dv_chunk = make_udiv(p.chunk);
   const size_t rows = (size_t)pr.B * pr.Hq * pr.Nq * p.nsplit;
   p.ws_o = static_cast<float*>(ws);
   p.ws_lse = p.ws_o + rows * pr.d;
