@@ -466,8 +466,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
   // same m for every wave (no test per load)
   constexpr int KL = KT / 1024;
   static_assert(KL % NW == 0 && LOADS == LW * NW, "even split of the loads");
-  auto issue_k = [&](auto slot_c, int u) {
-    const unsigned tb = (unsigned)(tile_of(u) * KT);
+  auto issue_k = [&](auto slot_c, int tile) {
+    const unsigned tb = (unsigned)(tile * KT);
 #pragma unroll
     for (int m = 0; m < KL / NW; ++m) {
       const int u2 = wave + NW * m;
@@ -475,8 +475,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
                              toffs[m] + tb, 0, 0, 0);
     }
   };
-  auto issue_v = [&](auto slot_c, int u) {
-    const unsigned tb = (unsigned)(tile_of(u) * KT);
+  auto issue_v = [&](auto slot_c, int tile) {
+    const unsigned tb = (unsigned)(tile * KT);
 #pragma unroll
     for (int m = KL / NW; m < LW; ++m) {
       const int u2 = wave + NW * m;
@@ -518,10 +518,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
   // softmax of tile t on its raw scores sc (skt, svt: the tile's K and V
   // scales): W = P * vr as E4M3 in wb (bytes 0..15: keys 16g + r, 16..31:
   // keys 32 + 16g + r), row sums in l
-  auto softmax = [&](int t, f32x16(&sc)[2], i32x8& wb, float skt,
+  auto softmax = [&](auto full_c, int t, f32x16(&sc)[2], i32x8& wb, float skt,
                      float svt) {
     const float cs = crow * skt;
-    if (!tile_full(t)) {
+    if (!decltype(full_c)::value && !tile_full(t)) {
       const int j0 = t * kBlk;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -602,9 +602,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
     // the wait for them is the end-of-step wait, not one in the softmax
     // behind the loads in flight
     float skc = skh[tile_of(0)], svc = svh[tile_of(0)];
-    issue_k(ic<0>(), 0);
-    issue_v(ic<0>(), 0);
-    if (1 < nt) issue_k(ic<1>(), 1);
+    issue_k(ic<0>(), tile_of(0));
+    issue_v(ic<0>(), tile_of(0));
+    if (1 < nt) issue_k(ic<1>(), tile_of(1));
     wait_vm0();
     barrier_nofence();
     if (wave_needs(tile_of(0))) qk(ic<0>(), sa);
@@ -615,26 +615,69 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
         skc = skh[tile_of(t + 1)];
         svc = svh[tile_of(t + 1)];
       }
-      if (t + 2 < nt) issue_k(ic<P>(), t + 2);
-      if (t + 1 < nt) issue_v(ic<1 - P>(), t + 1);
+      if (t + 2 < nt) issue_k(ic<P>(), tile_of(t + 2));
+      if (t + 1 < nt) issue_v(ic<1 - P>(), tile_of(t + 1));
       const int tt = tile_of(t);
       const bool need = wave_needs(tt);
       if (t + 1 < nt && wave_needs(tile_of(t + 1))) qk(ic<1 - P>(), sn);
       if (need) {
         i32x8 wb;
-        softmax(tt, sc, wb, skt, svt);
+        softmax(ic<0>(), tt, sc, wb, skt, svt);
         pv(ic<P>(), wb);
       }
       wait_vm0();
       barrier_nofence();
     };
-    // the loop leaves from inside the pair rather than skipping its second
+    // Interior steps [la, lb) of the longer run (the window run when there
+    // are two): tiles t and t + 1 are wholly allowed for every row of the
+    // wave and the tiles loaded in the step belong to the run.  Such a step
+    // is the one above with every decision known: tile t + toff, no mask
+    // test, no tests on the loads and the next tile's product.
+    int la = 0, lb = 0;
+    const int s0 = nt > nA ? nA : 0, s1 = nt > nA ? nt : nA;
+    const int toff = nt > nA ? tB0 - nA : 0;
+    if (wlive) {
+      const int f0 = (wl.lo + kBlk - 1) / kBlk;  // first tile left-full
+      const int f1 = wf.hw / kBlk;               // tiles below: right-full
+      la = max(s0, f0 - toff);
+      lb = min(s1 - 2, f1 - toff - 1);
+    }
+    auto lean = [&](auto par_c, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+      constexpr int P = decltype(par_c)::value;
+      const float skt = skc, svt = svc;
+      skc = skh[t + 1 + toff];
+      svc = svh[t + 1 + toff];
+      issue_k(ic<P>(), t + 2 + toff);
+      issue_v(ic<1 - P>(), t + 1 + toff);
+      qk(ic<1 - P>(), sn);
+      i32x8 wb;
+      softmax(ic<1>(), t + toff, sc, wb, skt, svt);
+      pv(ic<P>(), wb);
+      wait_vm0();
+      barrier_nofence();
+    };
+    // The loop leaves from inside the pair rather than skipping its second
     // step: the score buffers are dead after the loop, so the swap of roles
-    // costs no register copies at a join
-    for (int t = 0; t < nt; t += 2) {
+    // costs no register copies at a join.  The lean pairs run in a loop of
+    // their own, between the general steps before and after them.
+    const int lp0 = la + (la & 1);
+    const int lp1 = lp0 + 1 < lb ? lp0 + ((lb - lp0) & ~1) : lp0;
+    int t = 0;
+    for (; t < (lp1 > lp0 ? lp0 : nt); t += 2) {
       step(ic<0>(), t, sa, sb);
       if (t + 1 >= nt) break;
       step(ic<1>(), t + 1, sb, sa);
+    }
+    if (lp1 > lp0) {
+      for (; t < lp1; t += 2) {
+        lean(ic<0>(), t, sa, sb);
+        lean(ic<1>(), t + 1, sb, sa);
+      }
+      for (; t < nt; t += 2) {
+        step(ic<0>(), t, sa, sb);
+        if (t + 1 >= nt) break;
+        step(ic<1>(), t + 1, sb, sa);
+      }
     }
   }
 
