@@ -965,8 +965,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   for (int m = 0; m < TW; ++m) toffs[m] = tile_src_off<D>(wave + NW * m, lane);
   const auto krs = rows_rsrc(p.k + kv_base, s.L * D * 2);
   const auto vrs = rows_rsrc(p.v + kv_base, s.L * D * 2);
-  auto issue = [&](auto slot_c, int u) {
-    const int tb = tile_of(u) * kRT * D * 2;
+  auto issue = [&](auto slot_c, int tile) {
+    const int tb = tile * kRT * D * 2;
 #pragma unroll
     for (int m = 0; m < TW; ++m)
       miattn_buffer_load_lds(
@@ -979,9 +979,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
           toffs[m] + tb, 0, 0, 0);
   };
 
-  auto compute = [&](auto slot_c, int u) {
-    const int t = tile_of(u);
-    if (!wave_needs(t)) return;
+  // compute(full, slot, t): tile t's products; `full` (compile time) when
+  // every row of the wave sees the whole tile
+  auto compute = [&](auto full_c, auto slot_c, int t) {
+    constexpr bool FULL = decltype(full_c)::value != 0;
+    if (!FULL && !wave_needs(t)) return;
     const uint16_t* Kt = kslot(slot_c);
     const uint16_t* Vt = vslot(slot_c);
     // S^T = K Q^T and dP^T = V dO^T: lane (query, g) holds keys
@@ -991,9 +993,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const int j0 = t * kRT;
     f32x16 sa[2], pa[2];
     const f32x16 zero = {};
+    if constexpr (!FULL) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sa[mb] = zero;
-    if (!tile_full(t)) {
+      for (int mb = 0; mb < 2; ++mb) sa[mb] = zero;
+    }
+    if (!FULL && !tile_full(t)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -1021,8 +1025,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       constexpr int ks = i / 4, mb = (i / 2) % 2;
       if constexpr (i + 2 < NS) ring[(i + 2) % 3] = fetch(ic<i + 2>());
       if constexpr (i % 2 == 0)
-        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % 3], qf[ks],
-                                                         sa[mb], 0, 0, 0);
+        sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ring[i % 3], qf[ks], (FULL && ks == 0) ? zero : sa[mb], 0, 0, 0);
       else
         pa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             ring[i % 3], of[ks], ks == 0 ? zero : pa[mb], 0, 0, 0);
@@ -1077,19 +1081,53 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   };
 
   if (nt > 0) {
-    issue(ic<0>(), 0);
+    issue(ic<0>(), tile_of(0));
     wait_vm0();
     barrier_nofence();
     auto step = [&](auto slot_c, int u) {
       constexpr int S = decltype(slot_c)::value;
-      if (u + 1 < nt) issue(ic<1 - S>(), u + 1);
-      compute(slot_c, u);
+      if (u + 1 < nt) issue(ic<1 - S>(), tile_of(u + 1));
+      compute(ic<0>(), slot_c, tile_of(u));
       wait_vm0();
       barrier_nofence();
     };
-    for (int u = 0; u < nt; u += 2) {
+    // Interior steps [la, lb) of the longer run: every row of the wave sees
+    // the whole tile, and the next tile belongs to the run.  Such a step is
+    // the one above with every decision known (tile u + loff, no test, no
+    // mask, S started from the zero operand).
+    int la = 0, lb = 0;
+    const int s0 = nt > nA ? nA : 0, s1 = nt > nA ? nt : nA;
+    const int loff = nt > nA ? tB0 - nA : 0;
+    if (wlive) {
+      const int f0 = (wl.lo + kRT - 1) / kRT;  // first tile left-full
+      const int f1 = wf.hw / kRT;              // tiles below: right-full
+      la = max(s0, f0 - loff);
+      lb = min(s1 - 1, f1 - loff);
+    }
+    auto lean = [&](auto slot_c, int u) {
+      constexpr int S = decltype(slot_c)::value;
+      issue(ic<1 - S>(), u + 1 + loff);
+      compute(ic<1>(), slot_c, u + loff);
+      wait_vm0();
+      barrier_nofence();
+    };
+    // lean pairs in a loop of their own, between the general steps
+    const int lp0 = la + (la & 1);
+    const int lp1 = lp0 + 1 < lb ? lp0 + ((lb - lp0) & ~1) : lp0;
+    int u = 0;
+    for (; u < (lp1 > lp0 ? lp0 : nt); u += 2) {
       step(ic<0>(), u);
       if (u + 1 < nt) step(ic<1>(), u + 1);
+    }
+    if (lp1 > lp0) {
+      for (; u < lp1; u += 2) {
+        lean(ic<0>(), u);
+        lean(ic<1>(), u + 1);
+      }
+      for (; u < nt; u += 2) {
+        step(ic<0>(), u);
+        if (u + 1 < nt) step(ic<1>(), u + 1);
+      }
     }
   }
 
