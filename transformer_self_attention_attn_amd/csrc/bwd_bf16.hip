@@ -620,7 +620,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
     // three streams (pipeline fill and drain).
     auto phase = [&](auto sn_c, auto mn_c, auto sc_c, auto mc_c, auto sp_c,
                      auto mp_c, auto do_sdp_c, auto do_sm_c, auto do_kv_c,
-                     int tn) __attribute__((always_inline)) {
+                     auto full_c, int tn) __attribute__((always_inline)) {
+      constexpr bool FULLT = decltype(full_c)::value;  // tile tn known full
       constexpr int MN = decltype(mn_c)::value, MC = decltype(mc_c)::value;
       constexpr int MP = decltype(mp_c)::value;
       constexpr bool DO_SDP = decltype(do_sdp_c)::value;
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
   #pragma unroll
           for (int e = 0; e < 4; ++e) nd0[4 * q4 + e] = d4[e];
         }
-        if (!tile_full(tn)) {
+        if (!FULLT && !tile_full(tn)) {
           // rows 32 MN + 16 g + r of tile tn, allowed in [rlo, rhi)
           const int base = tn * kRT + MN * 32 + 16 * g;
           const int mlo = rlo - base, mhi = rhi - base;
@@ -769,37 +770,63 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(
       wait_vm0();
       __syncthreads();
       phase(ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), T(), F(), F(),
-            tile_of_step(0));
-      auto step = [&](auto s_c, int u) __attribute__((always_inline)) {
+            F(), tile_of_step(0));
+      // step u; `full` (compile time): tiles u and u + 1 are wholly allowed
+      // for every key of the wave and u + 2 < nsteps, so that neither phase
+      // builds a mask and the loads need no test
+      auto step = [&](auto s_c, auto full_c, int u)
+                      __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
         constexpr int S1 = (S + 1) % 3, S2 = (S + 2) % 3;
+        constexpr bool FULLS = decltype(full_c)::value;
         phase(ic<S>(), ic<1>(), ic<S>(), ic<0>(), ic<S2>(), ic<1>(), T(), T(),
-              T(), tile_of_step(u));
+              T(), full_c, tile_of_step(u));
         wait_vm0();
         barrier_nofence();
-        if (u + 2 < nsteps) issue(ic<S2>(), u + 2);
+        if (FULLS || u + 2 < nsteps) issue(ic<S2>(), u + 2);
         phase(ic<S1>(), ic<0>(), ic<S>(), ic<1>(), ic<S>(), ic<0>(), T(), T(),
-              T(), tile_of_step(u + 1));
+              T(), full_c, tile_of_step(u + 1));
       };
+      // The full tiles [f0, f1) are the steps [ua, ub) (tiles go down as u
+      // goes up); lean steps [la, lb), run in triples from a multiple of 3
+      // (the ring slot of step u is u % 3) in a loop of their own
+      const int f0 = (w_lo_max + kRT - 1) / kRT, f1 = w_hi_min / kRT;
+      const int ua = p.G * max(0, t_last - f1 + 1);
+      const int ub = p.G * max(0, t_last - f0 + 1);
+      const int la = ua, lb = min(ub - 1, nsteps - 2);
+      const int lp0 = (la + 2) / 3 * 3;
+      const int lp1 = lb - lp0 >= 3 ? lp0 + (lb - lp0) / 3 * 3 : lp0;
       int u = 0;
-      for (; u + 3 <= nsteps; u += 3) {
-        step(ic<0>(), u);
-        step(ic<1>(), u + 1);
-        step(ic<2>(), u + 2);
+      for (; u + 3 <= (lp1 > lp0 ? lp0 : nsteps); u += 3) {
+        step(ic<0>(), F(), u);
+        step(ic<1>(), F(), u + 1);
+        step(ic<2>(), F(), u + 2);
       }
-      if (u < nsteps) step(ic<0>(), u++);
-      if (u < nsteps) step(ic<1>(), u++);
+      if (lp1 > lp0) {
+        for (; u < lp1; u += 3) {
+          step(ic<0>(), T(), u);
+          step(ic<1>(), T(), u + 1);
+          step(ic<2>(), T(), u + 2);
+        }
+        for (; u + 3 <= nsteps; u += 3) {
+          step(ic<0>(), F(), u);
+          step(ic<1>(), F(), u + 1);
+          step(ic<2>(), F(), u + 2);
+        }
+      }
+      if (u < nsteps) step(ic<0>(), F(), u++);
+      if (u < nsteps) step(ic<1>(), F(), u++);
       // dKV(2n - 1): slot (n - 1) % 3
       const int sl = (nsteps - 1) % 3;
       if (sl == 0)
         phase(ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<0>(), ic<1>(), F(), F(), T(),
-              0);
+              F(), 0);
       else if (sl == 1)
         phase(ic<1>(), ic<0>(), ic<1>(), ic<0>(), ic<1>(), ic<1>(), F(), F(), T(),
-              0);
+              F(), 0);
       else
         phase(ic<2>(), ic<0>(), ic<2>(), ic<0>(), ic<2>(), ic<1>(), F(), F(), T(),
-              0);
+              F(), 0);
     }
   }
 
