@@ -119,6 +119,10 @@ BWD_SMALL = [
       window=65, sinks=4, len_lo=100, len_hi=500),
     W("bwd-d128-two-sided-padded", 2, 4, 2, 300, 300, 128, "bf16", False,
       window=40, window_right=70, len_lo=100, len_hi=300),
+    # wholly allowed tiles in a window run apart from the sink tiles (the
+    # kernels' steps without per-step tests, with the run's tile offset)
+    W("bwd-d128-wide-win-sinks-padded", 2, 4, 2, 900, 900, 128, "bf16", True,
+      window=400, sinks=70, len_lo=500, len_hi=900),
     W("bwd-d64-two-sided-sinks", 1, 4, 1, 333, 333, 64, "bf16", False,
       window=33, window_right=31, sinks=7),
     W("bwd-chunk-d128-padded", 2, 4, 2, 70, 300, 128, "bf16", True,

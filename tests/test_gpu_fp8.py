@@ -74,6 +74,9 @@ FP8_CASES = [
        window=65, sinks=4, len_lo=100, len_hi=400), True, False),
     (W("fp8-two-sided-d128", 1, 4, 1, 300, 300, 128, "bf16", False,
        window=40, window_right=70), True, False),
+    # wholly allowed tiles in a window run apart from the sink tiles
+    (W("fp8-wide-win-sinks-d128", 2, 4, 2, 1100, 1100, 128, "bf16", True,
+       window=400, sinks=70, len_lo=600, len_hi=1100), True, False),
     (W("fp8-outliers-d128", 2, 4, 2, 256, 256, 128, "bf16", True,
        outlier_channels=4, outlier_mag=20.0), True, False),
 ]

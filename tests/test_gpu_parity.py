@@ -238,6 +238,12 @@ MASK_SMALL = [
       window=100, sinks=65, len_lo=200, len_hi=520),
     W("causal-self-only-sinks-d128", 1, 4, 4, 300, 300, 128, "bf16", True,
       window=1, sinks=130),
+    # a window wide enough for wholly allowed tiles, apart from the sink
+    # tiles: the steps of the window run without per-step tests
+    W("causal-wide-win-sinks-d128", 2, 4, 2, 1100, 1100, 128, "bf16", True,
+      window=400, sinks=70, len_lo=600, len_hi=1100),
+    W("two-sided-wide-sinks-d128", 2, 4, 2, 700, 700, 128, "bf16", False,
+      window=300, window_right=260, sinks=9),
     W("sinks-past-window-d64", 2, 4, 2, 400, 400, 64, "bf16", True,
       window=50, sinks=200),
     # two-sided window with sinks, no causal mask
