@@ -48,14 +48,18 @@ MIATTN_HD constexpr int prefill_v_loads(int D) {
   return kTileRows * prefill_v_chunks(D) / 64;
 }
 // Byte offset within the source tile of lane `lane`'s part of load i.
+// (row and chunk from unsigned division: a multiply-high and a shift on the
+// device, where signed division by a constant needs sign fix-ups)
 MIATTN_HD constexpr unsigned prefill_k_src(int D, int i, int lane) {
-  const int s = i * 64 + lane, n = prefill_k_chunks(D);
-  const int r = s / n, c = s - (s / n) * n;
+  const unsigned s = (unsigned)(i * 64 + lane);
+  const unsigned n = (unsigned)prefill_k_chunks(D);
+  const int r = (int)(s / n), c = (int)(s % n);
   return 2u * (unsigned)(mfma_row(r) * D + (c < D / 8 ? c * 8 : 0));
 }
 MIATTN_HD constexpr unsigned prefill_v_src(int D, int i, int lane) {
-  const int s = i * 64 + lane, n = prefill_v_chunks(D);
-  const int r = s / n, c = s - (s / n) * n;
+  const unsigned s = (unsigned)(i * 64 + lane);
+  const unsigned n = (unsigned)prefill_v_chunks(D);
+  const int r = (int)(s / n), c = (int)(s % n);
   return 2u * (unsigned)(r * D + (c < D / 8 ? c * 8 : 0));
 }
 // Bytes of tile t's resource: its rows below the valid length L (0 for a

@@ -388,7 +388,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
 #pragma unroll
     for (int m = 0; m < C::KLW; ++m) {
       const int i = wave + NW * m;
-      if (i < C::KLOADS)
+      // (only a load number past NW (m + 1) can be out of range)
+      if (NW * (m + 1) <= C::KLOADS || i < C::KLOADS)
         miattn_buffer_load_lds(rs, (lds_void*)(kslot(slot_c) + i * 512), 16,
                                (int)kvo[m], 0, 0, 0);
     }
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
 #pragma unroll
     for (int m = 0; m < C::VLW; ++m) {
       const int i = wave + NW * m;
-      if (i < C::VLOADS)
+      if (NW * (m + 1) <= C::VLOADS || i < C::VLOADS)
         miattn_buffer_load_lds(rs, (lds_void*)(vslot(slot_c) + i * 512), 16,
                                (int)vvo[m], 0, 0, 0);
     }
