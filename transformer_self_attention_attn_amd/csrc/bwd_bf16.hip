@@ -48,7 +48,10 @@
 // half of the tile runs between the MFMAs of the other half; at d=128 the
 // halves pass through a three-stream pipeline (products of the next half,
 // softmax of this one, gradient products of the previous one), so that the
-// exponentials spread over every MFMA of the step.
+// exponentials spread over every MFMA of the step.  In both gradient kernels
+// the steps whose tiles every row (or key) of the wave fully sees run in a
+// loop of their own, with no mask construction or per-step test; bwd_dq
+// deals its blocks in the forward kernels' order (block_order.h).
 #include "kernels.h"
 
 #include <cmath>

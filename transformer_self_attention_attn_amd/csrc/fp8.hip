@@ -44,7 +44,10 @@
 // operand reads are free of bank conflicts.  Workgroups of 4 wavefronts (128
 // query rows), two per CU: their barriers are independent, so the two waves
 // on each SIMD drift out of phase and one's softmax overlaps the other's
-// matrix products (one 8-wavefront workgroup per CU ran 12% slower).
+// matrix products (one 8-wavefront workgroup per CU ran 12% slower).  Blocks
+// are dealt to the XCDs in the bf16 kernel's order (block_order.h), and the
+// steps in which a wave needs all of two consecutive tiles run in a loop of
+// their own, with no per-step test.
 #include "kernels.h"
 
 #include <cmath>

@@ -21,10 +21,12 @@
 //   the workgroup may see (tiles entirely above the causal diagonal, left of
 //   the window or past the valid length are never loaded); a wave skips the
 //   arithmetic of tiles that none of its rows may see, and only tiles that
-//   are partly allowed pay for per-element masking.  Query heads of one K/V
-//   head are adjacent in the launch order and the block index is remapped so
-//   that each XCD (own L2) works on a contiguous range of (batch, K/V head)
-//   groups; causal blocks run heaviest first.
+//   are partly allowed pay for per-element masking.  The steps in which a
+//   wave needs all of a tile and both tiles it loads are whole run in a loop
+//   of their own, with every one of these decisions known (no per-step
+//   test).  Query heads of one K/V head are adjacent in the launch order and
+//   the block index is remapped so that each XCD (own L2) runs whole (batch,
+//   K/V head) groups, causal blocks heaviest first (block_order.h).
 //
 // Data movement
 //   K and V tiles go from HBM straight into LDS with 16-byte direct-to-LDS
@@ -64,7 +66,7 @@
 // workgroups share each CU (LDS and registers are sized for it), so every
 // SIMD runs wavefronts of two workgroups whose barriers are independent: they
 // drift apart and one wave's X overlaps the other's Y without any offset
-// imposed inside a workgroup.
+// imposed inside a workgroup (three workgroups per CU at d = 64).
 #include "kernels.h"
 
 #include <cmath>
