@@ -21,6 +21,11 @@ __device__ void miattn_buffer_load_lds(
     miattn_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
     int voffset, int soffset, int offset,
     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// The 16-byte buffer load into registers, declared the same way: a lane's
+// bytes at or past the resource's end read as zeros.
+__device__ miattn_i32x4 miattn_buffer_load_b128(
+    miattn_i32x4 rsrc, int voffset, int soffset,
+    int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
 namespace miattn {
 namespace dev {

@@ -333,23 +333,18 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   };
 
   // ---- Q^T fragments (B operand), kept in registers -----------------------
+  // Read through a resource that ends at the live rows (Lq rows of the
+  // head): a dead row reads as zeros, with no branch per load.  The sign of
+  // a negative scale is applied just before the first product, so that
+  // nothing waits for these loads before then.
   bf16x8 qf[C::KS];
+  {
+    const miattn_i32x4 qrs = dev::rows_rsrc(p.q + qo_base, Lq * D * 2);
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qlive) {
-      raw = *reinterpret_cast<const u32x4*>(p.q + qo_base + (size_t)qi * D +
-                                            16 * ks + 8 * g);
-    }
-    qf[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-  if (p.qsign != 0) {  // negative scale: Q negated (uniform branch)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 raw = __builtin_bit_cast(u32x4, qf[ks]);
-      raw ^= p.qsign;
-      qf[ks] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[ks] = __builtin_bit_cast(
+          bf16x8, miattn_buffer_load_b128(qrs, (qi * D + 16 * ks + 8 * g) * 2,
+                                          0, 0));
   }
 
   // ---- direct-to-LDS tile loads ---------------------------------------------
@@ -641,6 +636,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     dma_k(ic<0>(), tile_of(0));
     dma_v(ic<0>(), tile_of(0));
     if (1 < nt) dma_k(ic<1>(), tile_of(1));
+  }
+  if (p.qsign != 0) {  // negative scale: Q negated (uniform branch)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 raw = __builtin_bit_cast(u32x4, qf[ks]);
+      raw ^= p.qsign;
+      qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
   }
   wait_vmcnt(0);
   barrier_nofence();
