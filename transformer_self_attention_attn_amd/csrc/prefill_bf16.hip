@@ -206,10 +206,19 @@ struct PrefillParams {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
-template <int D, int NW>
+// Mask kinds, one kernel each so that the masked tile's code has one path
+// (a run-time choice among three made the compiler copy every score at the
+// join): keys below a right limit only (look-ahead, padding, right window),
+// a left window as well, and attention sinks as well.
+enum MaskKind { kMaskRight = 0, kMaskWindow = 1, kMaskSinks = 2 };
+
+template <int D, int NW, int MK>
 __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     PrefillParams p) {
   using C = Cfg<D, NW>;
+  // the left window and the sink count, 0 where the kind has none
+  const int window = MK == kMaskRight ? 0 : p.window;
+  const int sinks = MK == kMaskSinks ? p.sinks : 0;
   // one LDS object per ring slot: the compiler keeps per-object alias
   // scopes, which lets reads of one slot proceed while another is filled
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[C::KTILE];
@@ -280,12 +289,12 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     return p.window_right > 0 ? max(0, min(h, rpos + p.window_right)) : h;
   };
   auto left = [&](int rpos) {
-    return p.window > 0 ? max(0, rpos - p.window + 1) : 0;
+    return window > 0 ? max(0, rpos - window + 1) : 0;
   };
   const int hc = qlive ? cap(pos) : 0;
   const int hw = right(pos, hc);
   const int lo = qlive ? left(pos) : 0;
-  const int sk = min(p.sinks, hc);
+  const int sk = min(sinks, hc);
 
   // Tiles the workgroup visits: the sink tiles [0, ts1), then the window
   // tiles [tw0, tw1) (merged into one run when they meet).  Step k of the
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     const int kv_lo = left(q0 + off);
     int tw0 = kv_lo / kKT, tw1 = (kv_hi + kKT - 1) / kKT;
     if (kv_hi <= kv_lo) tw0 = tw1 = 0;
-    const int ts1 = (min(p.sinks, kv_hc) + kKT - 1) / kKT;
+    const int ts1 = (min(sinks, kv_hc) + kKT - 1) / kKT;
     if (ts1 >= tw0) {
       nA = max(ts1, tw1);
       nt = nA;
@@ -320,8 +329,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   const int w_hi_max = right(wpl, w_hc_max);
   const int w_hi_min = right(wpf, w_hc_min);
   const int w_lo_min = left(wpf), w_lo_max = left(wpl);
-  const int w_sk_max = min(p.sinks, w_hc_max);
-  const int w_sk_min = min(p.sinks, w_hc_min);
+  const int w_sk_max = min(sinks, w_hc_max);
+  const int w_sk_min = min(sinks, w_hc_min);
   auto wave_needs = [&](int t) {
     const int j0 = t * kKT;
     return wlive &&
@@ -458,7 +467,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
     if (!FULL && !tile_full(t)) {
       // this lane's keys of block mb are jb + r, r = 0 .. 15; the bounds are
       // taken relative to jb so that each test compares with a constant r
-      if (p.window == 0 && p.sinks == 0) {  // keys below hw only
+      if constexpr (MK == kMaskRight) {  // keys below hw only
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const int hi = hw - (j0 + mb * 32 + g * 16);
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
           for (int r = 0; r < 16; ++r)
             if (r >= hi) sc[mb][r] = -INFINITY;
         }
-      } else if (p.sinks == 0) {  // keys in [lo, hw)
+      } else if constexpr (MK == kMaskWindow) {  // keys in [lo, hw)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const int jb = j0 + mb * 32 + g * 16;
@@ -766,7 +775,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int MK>
 void launch(const PrefillParams& p0, hipStream_t stream) {
   using C = Cfg<D, NW>;
   PrefillParams p = p0;
@@ -778,7 +787,7 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
   // first across the XCD's groups)
   p.order = make_block_order(p.B, p.Hkv, p.G, p.nqb, p.causal != 0,
                              2LL * p.Nk * D * 2, 32 * (D == 64 ? 3 : 2));
-  hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3(p.total),
+  hipLaunchKernelGGL((prefill_kernel<D, NW, MK>), dim3(p.total),
                      dim3(C::THREADS), 0, stream, p);
 }
 
@@ -810,10 +819,16 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
   // weight 2^(s*c - m) still rounds to exactly 1.0f, as with c = 0.
   if (p.c == 0.f) p.c = 1e-30f;
   p.qsign = (pr.scale < 0.f) ? 0x80008000u : 0u;
-  if (pr.d == 128)
-    launch<128, MIATTN_PREFILL_NW128>(p, stream);
-  else
-    launch<64, MIATTN_PREFILL_NW64>(p, stream);
+  const int mk = p.sinks > 0 ? kMaskSinks : p.window > 0 ? kMaskWindow : kMaskRight;
+  if (pr.d == 128) {
+    if (mk == kMaskRight) launch<128, MIATTN_PREFILL_NW128, kMaskRight>(p, stream);
+    else if (mk == kMaskWindow) launch<128, MIATTN_PREFILL_NW128, kMaskWindow>(p, stream);
+    else launch<128, MIATTN_PREFILL_NW128, kMaskSinks>(p, stream);
+  } else {
+    if (mk == kMaskRight) launch<64, MIATTN_PREFILL_NW64, kMaskRight>(p, stream);
+    else if (mk == kMaskWindow) launch<64, MIATTN_PREFILL_NW64, kMaskWindow>(p, stream);
+    else launch<64, MIATTN_PREFILL_NW64, kMaskSinks>(p, stream);
+  }
   return hipGetLastError();
 }
 
