@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "block_order.h"
+#include "tail_queue.h"
 
 using namespace miattn;
 
@@ -95,6 +96,36 @@ static void check_shape(int B, int Hkv, int G, int nqb, bool causal,
           G, nqb, k, seen[k]);
 }
 
+// The run-time tail of tail_queue.h: the fixed blocks (ids below first, the
+// first three quarters of every XCD's list) and the blocks of tickets
+// 0 .. ndyn-1 (id first + ticket while below total) cover every block once,
+// with enough dynamic workgroups for the whole tail; off, the grid is the
+// block count.
+static void check_tail(int total, int slots, bool on, bool expect_on) {
+  int grid = -1;
+  const TailQueue q = make_tail_queue(total, slots, on, &grid);
+  if (!expect_on) {
+    CHECK(q.first == total && q.ndyn == 0 && grid == total,
+          "tail total=%d: expected off, first=%d ndyn=%d grid=%d", total,
+          q.first, q.ndyn, grid);
+    return;
+  }
+  CHECK(q.first % kTailXcds == 0 && q.first < total,
+        "tail total=%d: first=%d", total, q.first);
+  CHECK(q.first / kTailXcds == total / kTailXcds - total / kTailXcds / 4,
+        "tail total=%d: split slot %d", total, q.first / kTailXcds);
+  CHECK(grid >= total && q.ndyn == grid - q.first && q.ndyn >= total - q.first,
+        "tail total=%d: grid=%d ndyn=%d", total, grid, q.ndyn);
+  CHECK(q.set >= 0 && q.set < kTailSets, "tail set %d", q.set);
+  std::vector<int> seen(total, 0);
+  for (int b = 0; b < q.first; ++b) seen[b]++;
+  for (int t = 0; t < q.ndyn; ++t)
+    if (q.first + t < total) seen[q.first + t]++;
+  for (int b = 0; b < total; ++b)
+    CHECK(seen[b] == 1, "tail total=%d: block %d run %d times", total, b,
+          seen[b]);
+}
+
 int main() {
   check_shape(4, 4, 7, 32, true, 2LL << 20, 64);     // gqa-causal-prefill
   check_shape(16, 12, 1, 8, true, 256LL << 10, 96);  // gpt2-small-causal-padded
@@ -103,6 +134,11 @@ int main() {
   check_shape(2, 4, 4, 10, false, 4LL << 20, 64);    // no causal mask
   check_shape(8, 8, 16, 64, true, 4LL << 20, 64);    // bands of several blocks
   check_shape(1, 1, 1, 1, true, 1024, 64);           // one block
+  check_tail(4 * 4 * 7 * 32, 64, true, true);    // gqa-causal-prefill
+  check_tail(8 * 8 * 16 * 64, 64, true, true);   // many blocks
+  check_tail(3 * 8 * 64 + 5, 64, true, true);    // not a multiple of 8
+  check_tail(16 * 12 * 8, 96, true, false);      // under three rounds
+  check_tail(2 * 16 * 128, 96, false, false);    // not asked for
   if (g_fails) {
     std::printf("%d failures\n", g_fails);
     return 1;

@@ -3,7 +3,8 @@
 tests/block_order_check.cpp maps every block id of seven shapes and checks
 that the map is a bijection onto (batch, K/V head, head, query block), that
 it equals a plain-division reference, and, on the longest-first path, that a
-group stays on one XCD and each band runs heaviest first.  Planted mistakes
+group stays on one XCD and each band runs heaviest first; and that the
+run-time tail of tail_queue.h runs every block once.  Planted mistakes
 in a copy of the header must make it fail.
 """
 
@@ -26,6 +27,7 @@ def build_and_run(tmp_path, header_text=None):
     inc = str(tmp_path / "inc")
     os.makedirs(inc, exist_ok=True)
     shutil.copy(os.path.join(CSRC, "fastdiv.h"), inc)
+    shutil.copy(os.path.join(CSRC, "tail_queue.h"), inc)
     with open(os.path.join(inc, "block_order.h"), "w") as f:
         f.write(HEADER if header_text is None else header_text)
     exe = str(tmp_path / "block_order_check")

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import synth
+import transformer_self_attention_attn_amd as mi
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -314,6 +315,29 @@ def test_nan_padding_is_never_read(w):
     assert torch.isfinite(ob.float()).all()
     assert torch.equal(oa, ob)
     assert torch.equal(la, lb)
+
+
+def test_tail_queue_every_launch():
+    """A causal launch of several rounds of the chip's workgroup slots takes
+    each XCD's lightest query blocks from a run-time queue whose counters the
+    launch zeroes again as it ends.  Over launches in a row, with the outputs
+    filled with NaN before each, every row is written every time and the
+    results are bitwise the same."""
+    w = synth.by_name("gqa-causal-prefill")
+    gu.say(f"[gpu] tail queue {w.name}")
+    q, k, v, sl = gu.to_dev(synth.make_inputs(w, 3))
+    ref = None
+    for _ in range(4):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32,
+                         device=q.device)
+        mi.attn(q, k, v, causal=True, seqlens=sl, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        if ref is None:
+            ref = (o, lse)
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
 
 
 def test_deterministic_bitwise():

@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "block_order.h"
+#include "tail_queue.h"
 #include "device_common.h"
 
 namespace miattn {
@@ -304,6 +305,7 @@ struct Fp8Params {
   float c;  // |scale| * log2(e) (divided by d for rotated operands)
   unsigned qsign;  // 0x80808080 when the scale is negative: Q codes negated
   BlockOrder order;  // block -> (batch, head, query block): block_order.h
+  TailQueue tail;    // lightest blocks handed out at run time: tail_queue.h
 };
 
 template <int D, int NW>
@@ -327,8 +329,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
   };
 
   // block -> (batch, K/V head, query block, head of the group): the order
-  // of block_order.h (whole groups per XCD, causal blocks heaviest first)
-  const BlockPos bpos = block_pos(blockIdx.x, p.order);
+  // of block_order.h (whole groups per XCD, causal blocks heaviest first);
+  // from p.tail.first on, the workgroups take the lightest blocks from the
+  // run-time queue of tail_queue.h
+  int bid = blockIdx.x;
+  unsigned tail_done = 0;
+  if (bid >= p.tail.first) {
+    __shared__ int s_bid;
+    if (threadIdx.x == 0) s_bid = tail_take(p.tail, p.order.total, &tail_done);
+    __syncthreads();
+    bid = s_bid;
+    if (bid < 0) {
+      if (threadIdx.x == 0) tail_clear(p.tail, tail_done);
+      return;
+    }
+  }
+  const BlockPos bpos = block_pos(bid, p.order);
   const int qb = bpos.qb;
   const int b = bpos.b;
   const int hk = bpos.hk;
@@ -704,6 +720,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fp8_kernel(Fp8Params p) {
       p.lse[bhq * p.Nq + qi] =
           any ? (M + log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
+  if (blockIdx.x >= p.tail.first && threadIdx.x == 0)
+    tail_clear(p.tail, tail_done);
 }
 
 template <int D>
@@ -832,11 +850,18 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
   // K and V^T codes of one group: 2 Nkp d bytes; two workgroups per CU
   p.order = make_block_order(pr.B, pr.Hkv, p.G, p.nqb, pr.causal != 0,
                              2LL * p.Nkp * pr.d, 32 * 2);
+  // the run-time tail: causal longest-first order with no left window or
+  // sinks (so that the last blocks are the light ones)
+  int grid = p.total;
+  p.tail = make_tail_queue(p.total, 32 * 2,
+                           p.order.lpt && p.order.causal && pr.window == 0 &&
+                               pr.sinks == 0,
+                           &grid);
   if (pr.d == 128)
-    hipLaunchKernelGGL((attn_fp8_kernel<128, NW>), dim3(p.total),
+    hipLaunchKernelGGL((attn_fp8_kernel<128, NW>), dim3(grid),
                        dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fp8_kernel<64, NW>), dim3(p.total),
+    hipLaunchKernelGGL((attn_fp8_kernel<64, NW>), dim3(grid),
                        dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }

@@ -74,6 +74,7 @@
 
 #include "device_common.h"
 #include "block_order.h"
+#include "tail_queue.h"
 
 // Workgroup shape per head dimension, chosen by measurement on MI355X: both
 // run 4 wavefronts (128 query rows share each K/V tile) with at least two
@@ -201,6 +202,7 @@ struct PrefillParams {
   float c;         // |scale| * log2(e) (a tiny positive value for scale 0)
   unsigned qsign;  // 0x80008000 when scale < 0: Q is negated on load
   BlockOrder order;  // block -> (batch, head, query block): block_order.h
+  TailQueue tail;    // lightest blocks handed out at run time: tail_queue.h
 };
 
 template <int I>
@@ -239,8 +241,21 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
 
   // ---- block -> (batch, head, query block) --------------------------------
   // the order of block_order.h: whole (batch, K/V head) groups per XCD,
-  // causal blocks heaviest first
-  const BlockPos bpos = block_pos(blockIdx.x, p.order);
+  // causal blocks heaviest first; from p.tail.first on, the workgroups take
+  // the lightest blocks from the run-time queue of tail_queue.h
+  int bid = blockIdx.x;
+  unsigned tail_done = 0;
+  if (bid >= p.tail.first) {
+    __shared__ int s_bid;
+    if (threadIdx.x == 0) s_bid = tail_take(p.tail, p.order.total, &tail_done);
+    __syncthreads();
+    bid = s_bid;
+    if (bid < 0) {
+      if (threadIdx.x == 0) tail_clear(p.tail, tail_done);
+      return;
+    }
+  }
+  const BlockPos bpos = block_pos(bid, p.order);
   const int qb = bpos.qb;
   const int b = bpos.b;
   const int hk = bpos.hk;
@@ -773,6 +788,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void prefill_kernel(
           any ? (M + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
+  if (blockIdx.x >= p.tail.first && threadIdx.x == 0)
+    tail_clear(p.tail, tail_done);
 }
 
 template <int D, int NW, int MK>
@@ -785,9 +802,16 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
   // the smallest divisor of nqb whose band of one group (qband * G blocks)
   // fills an XCD's workgroup slots (32 CUs); otherwise 1 (plain heaviest
   // first across the XCD's groups)
+  constexpr int kSlots = 32 * (D == 64 ? 3 : 2);  // workgroups per XCD at once
   p.order = make_block_order(p.B, p.Hkv, p.G, p.nqb, p.causal != 0,
-                             2LL * p.Nk * D * 2, 32 * (D == 64 ? 3 : 2));
-  hipLaunchKernelGGL((prefill_kernel<D, NW, MK>), dim3(p.total),
+                             2LL * p.Nk * D * 2, kSlots);
+  // the run-time tail: causal longest-first order with no left window (so
+  // that the last blocks are the light ones)
+  int grid = p.total;
+  p.tail = make_tail_queue(p.total, kSlots,
+                           p.order.lpt && p.order.causal && MK == kMaskRight,
+                           &grid);
+  hipLaunchKernelGGL((prefill_kernel<D, NW, MK>), dim3(grid),
                      dim3(C::THREADS), 0, stream, p);
 }
 
