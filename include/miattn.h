@@ -65,6 +65,15 @@
  * their kernels must not overlap: issue them on one stream, or order the
  * streams.
  *
+ * Run-time tail: a causal prefill (attn_fwd, attn_fwd_masked with no left
+ * window) or attn_fwd_fp8 of at least three rounds of the chip's workgroup
+ * slots takes its lightest query blocks from a device-wide ticket counter,
+ * one counter set per call from a ring of 64 per device (a captured graph
+ * keeps the set of its capture); the call's last workgroup to take a ticket
+ * zeroes the set.  Such calls on one device whose kernels overlap in time
+ * and hold the same set would race, so no more than 64 of them may run at
+ * once on one device.
+ *
  * Errors: the return value is a status.  Argument checks run on the host
  * before any HIP call, so they are testable without a GPU.  No call aborts or
  * throws.  attn_last_error() describes the most recent non-OK status of the
