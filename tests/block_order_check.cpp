@@ -103,7 +103,7 @@ static void check_shape(int B, int Hkv, int G, int nqb, bool causal,
 // block count.
 static void check_tail(int total, int slots, bool on, bool expect_on) {
   int grid = -1;
-  const TailQueue q = make_tail_queue(total, slots, on, &grid);
+  const TailQueue q = make_tail_queue(total, slots, 3, on, &grid);
   if (!expect_on) {
     CHECK(q.first == total && q.ndyn == 0 && grid == total,
           "tail total=%d: expected off, first=%d ndyn=%d grid=%d", total,

@@ -853,7 +853,7 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
   // the run-time tail: causal longest-first order with no left window or
   // sinks (so that the last blocks are the light ones)
   int grid = p.total;
-  p.tail = make_tail_queue(p.total, 32 * 2,
+  p.tail = make_tail_queue(p.total, 32 * 2, 3,
                            p.order.lpt && p.order.causal && pr.window == 0 &&
                                pr.sinks == 0,
                            &grid);

@@ -808,7 +808,7 @@ void launch(const PrefillParams& p0, hipStream_t stream) {
   // the run-time tail: causal longest-first order with no left window (so
   // that the last blocks are the light ones)
   int grid = p.total;
-  p.tail = make_tail_queue(p.total, kSlots,
+  p.tail = make_tail_queue(p.total, kSlots, 3,
                            p.order.lpt && p.order.causal && MK == kMaskRight,
                            &grid);
   hipLaunchKernelGGL((prefill_kernel<D, NW, MK>), dim3(grid),

@@ -1,4 +1,4 @@
-// A run-time queue for the light tail of a causal forward launch.
+// A run-time queue for the light tail of a causal launch.
 // Internal; not installed.
 //
 // The hardware deals workgroups to the 8 XCDs round-robin, a fixed share
@@ -40,15 +40,16 @@ struct TailQueue {
 
 // The queue of a launch of `total` blocks; *grid receives the launch's
 // workgroup count.  Off (grid = total) unless `on` and the launch fills the
-// chip's slots three times or more.
-inline TailQueue make_tail_queue(int total, int slots_per_xcd, bool on,
-                                 int* grid) {
+// chip's slots min_rounds times or more.
+inline TailQueue make_tail_queue(int total, int slots_per_xcd, int min_rounds,
+                                 bool on, int* grid) {
   static std::atomic<unsigned> next_set{0};
   TailQueue q{total, 0, 0};
   *grid = total;
   const int n_min = total / kTailXcds;  // blocks of the shortest list
   const int dyn = n_min / 4;            // tail blocks per XCD
-  if (!on || total < 3 * kTailXcds * slots_per_xcd || dyn < 4) return q;
+  if (!on || total < min_rounds * kTailXcds * slots_per_xcd || dyn < 4)
+    return q;
   q.first = kTailXcds * (n_min - dyn);
   *grid = total + kTailXcds * (dyn / 4);
   q.ndyn = *grid - q.first;
