@@ -57,9 +57,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
+_CSRC = "transformer_self_attention_attn_amd/csrc/"
+# each kernel's source and the local headers it is built from
 KERNEL_SOURCES = {
-    "prefill": "transformer_self_attention_attn_amd/csrc/prefill_bf16.hip",
-    "decode": "transformer_self_attention_attn_amd/csrc/decode_bf16.hip",
+    "prefill": tuple(_CSRC + f for f in (
+        "prefill_bf16.hip", "kernels.h", "device_common.h", "lane_layout.h",
+        "block_order.h", "fastdiv.h", "tail_queue.h")),
+    "decode": tuple(_CSRC + f for f in (
+        "decode_bf16.hip", "kernels.h", "device_common.h", "lane_layout.h",
+        "fastdiv.h")),
 }
 
 
@@ -120,9 +126,13 @@ def trimmed(ms):
                 min_ms=s[0], reps=n)
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(rels):
+    """sha256 over the files' bytes, in order."""
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(kind):
