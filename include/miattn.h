@@ -97,7 +97,11 @@ enum miattn_status {
                                    window > 0 without causal; attn_bwd and
                                    the FP8 calls: one sequence (Nq rows, or
                                    Nk rows padded to 64, of d bf16) spanning
-                                   2^31 bytes or more */
+                                   2^31 bytes or more; attn_fwd(_masked)
+                                   calls that take the prefill kernel (every
+                                   call but Nq == 1 and short chunks): Nq
+                                   rows of d bf16 spanning 2^31 bytes or
+                                   more */
   MIATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
   MIATTN_ERR_NOMEM = -4         /* the workspace could not be grown */
 };

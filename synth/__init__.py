@@ -7,4 +7,4 @@ recipe.
 """
 
 from .workloads import WORKLOADS, Workload, by_name  # noqa: F401
-from .gen import make_dout, make_inputs, make_signs  # noqa: F401
+from .gen import device_normal, make_dout, make_inputs, make_signs  # noqa: F401

@@ -15,6 +15,10 @@ Generator(PCG64([seed, 1])): float32 standard normals of the query shape,
 cast the same way.
 Optionally the padded region (keys at or beyond the valid length, query rows
 beyond the live rows) is overwritten with NaN to prove outputs never read it.
+Inputs too large to draw on the host (sequences of millions of rows) come
+from `device_normal`: torch's Philox generator on the device, seeded with
+the given seed, float32 standard normals cast to the storage dtype; only the
+rows a check needs are copied back.
 """
 
 import numpy as np
@@ -90,3 +94,17 @@ def make_signs(d, seed):
     entries +1 / -1 (int8), from Generator(PCG64([seed, 2]))."""
     rng = np.random.Generator(np.random.PCG64([seed, 2]))
     return rng.choice(np.array([-1, 1], dtype=np.int8), size=d)
+
+
+def device_normal(shape, seed, device, dtype=torch.bfloat16):
+    """float32 standard normals of `shape` drawn on `device` from
+    torch.Generator(device).manual_seed(seed), cast to `dtype` (round to
+    nearest even) one slice of the leading dimension at a time, so that the
+    float32 draw of only one slice is held at once."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for i in range(shape[0]):
+        out[i] = torch.randn(shape[1:], generator=g, device=device,
+                             dtype=torch.float32).to(dtype)
+    return out

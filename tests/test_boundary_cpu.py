@@ -226,3 +226,17 @@ def test_backward_rejects_sequences_past_one_resource(Nq, Nk, d):
     rc = call_bwd(good(B=1, Hq=1, Hkv=1, Nq=Nq, Nk=Nk, d=d))
     assert rc == mi.MIATTN_ERR_UNSUPPORTED
     assert "2^31" in mi.attn_last_error()
+
+
+@pytest.mark.parametrize("fn_name", ["attn_fwd", "attn_fwd_masked"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_sequence_of_2gib_rejected_on_host(fn_name, d):
+    """The prefill kernel addresses a head's query rows with 32-bit byte
+    offsets: Nq rows of d bf16 must span less than 2^31 bytes."""
+    fn = getattr(mi, fn_name)
+    n = (1 << 31) // (2 * d)  # exactly 2^31 bytes of query rows
+    a = good(B=1, Hq=1, Hkv=1, Nq=n, Nk=n, d=d)
+    rc = call(fn, a) if fn_name == "attn_fwd" else call_masked(fn, a)
+    assert rc == mi.MIATTN_ERR_UNSUPPORTED
+    err = mi.attn_last_error()
+    assert fn_name in err and "2^31" in err, err

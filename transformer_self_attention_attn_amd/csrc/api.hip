@@ -161,6 +161,13 @@ int run_bf16(const char* fn, const void* q, const void* k, const void* v,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   int rc;
+  // the prefill kernel reads a head's query rows through one 32-bit buffer
+  // resource, with 32-bit byte offsets: they must span less than 2^31 bytes
+  // (the decode kernel's offsets are 64-bit)
+  if (!miattn::decode_takes(p) && (long long)p.Nq * p.d * 2 >= (1LL << 31))
+    return fail(MIATTN_ERR_UNSUPPORTED,
+                "%s: one sequence of Nq=%d query rows at d=%d spans 2^31 "
+                "bytes or more", fn, p.Nq, p.d);
   if (miattn::decode_takes(p)) {
     std::lock_guard<std::mutex> lock(g_ws_mu);
     void* ws = nullptr;
