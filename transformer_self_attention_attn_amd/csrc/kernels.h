@@ -19,7 +19,8 @@ struct Problem {
   const int* seqlens;  // device pointer or nullptr
 };
 
-// Tiled bf16 MFMA prefill (Nq == Nk).
+// Tiled bf16 MFMA prefill: Nq == Nk, and 1 < Nq < Nk (chunks against a
+// cache, cross-attention) where decode_takes is false.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v,
                                void* o, float* lse, const Problem& p,
                                hipStream_t stream);
@@ -53,7 +54,7 @@ hipError_t launch_fwd_fp8(const void* q8, const float* sq, const void* k8,
                           void* o, float* lse, const Problem& p, int rotated,
                           hipStream_t stream);
 
-// fp32 path (any Nq in {1, Nk}).
+// fp32 path (any 1 <= Nq <= Nk).
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v,
                            float* o, float* lse, const Problem& p,
                            hipStream_t stream);
