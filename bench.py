@@ -451,7 +451,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus "
-              f"{args.gpus}); this build has no multi-GPU path.",
+              f"{args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     if args.only:
