@@ -69,3 +69,44 @@ def test_graph_replays_match_eager():
         for (w, _), (o, lse), (ro, rl) in zip(specs, eager, ref):
             assert torch.equal(o, ro), f"eager {rep}: {w.name} o differs"
         gu.say(f"  replay {rep}: bitwise equal to the eager calls")
+
+
+def test_graph_backward_and_fp8_match_eager():
+    """The backward pass (workspace, three launches) and the FP8 path
+    (quantizer, then the forward on the codes with its run-time tail) of
+    the headline prefill, captured and replayed the same way; the tensors
+    a call allocates during the capture come from the graph's own pool and
+    each replay rewrites them."""
+    w = synth.by_name("gqa-causal-prefill")
+    x = synth.make_inputs(w, 3)
+    q, k, v, _ = gu.to_dev(x)
+    dout = synth.make_dout(w, 3)[0].to(gu.DEV)
+    signs = torch.from_numpy(synth.make_signs(w.d, 3)).to(gu.DEV)
+    gu.say("[gpu] graph: backward and FP8 on gqa-causal-prefill")
+    o, lse = mi.attn(q, k, v, causal=True)
+
+    def calls():
+        grads = mi.attn_backward(q, k, v, o, lse, dout, causal=True)
+        z = mi.fp8_quantize(q, k, v, signs=signs)
+        o8, l8 = mi.attn_fp8(z, causal=True)
+        return grads + (o8, l8)
+
+    ref = calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        got = calls()
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "o8", "lse8")
+    for rep in range(3):
+        for t in got:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(names, got, ref):
+            assert torch.equal(t, r), f"replay {rep}: {name} differs"
+        again = calls()
+        torch.cuda.synchronize()
+        for name, t, r in zip(names, again, ref):
+            assert torch.equal(t, r), f"eager {rep}: {name} differs"
+        gu.say(f"  replay {rep}: bitwise equal to the eager calls")
