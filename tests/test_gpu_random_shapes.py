@@ -1,0 +1,57 @@
+"""GPU parity on a seeded sweep of shapes and masks drawn at random, every
+row against the oracle: head dimension, dtype, group size, Nq (= Nk, 1, or
+in between), Nk, causal or not, left and right window limits, sink keys,
+valid lengths and amplitude.  The draws come from one fixed generator, so
+the sweep is the same on every run; each case prints its shape first.
+Sizes are capped so that the whole sweep's oracle work stays within
+seconds.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 192
+
+
+def _draw_cases(seed=20261204, n=N_CASES):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        dtype = "fp32" if rng.random() < 0.15 else "bf16"
+        hkv = int(rng.choice([1, 2, 3]))
+        g = int(rng.choice([1, 2, 3, 4, 7, 8]))
+        nk = int(rng.integers(1, 700))
+        kind = rng.random()
+        nq = nk if kind < 0.55 else (1 if kind < 0.75 else
+                                    int(rng.integers(1, nk + 1)))
+        b = int(rng.integers(1, 4))
+        if b * hkv * g * nq * nk * d > 1.5e8:  # oracle time
+            continue
+        causal = bool(rng.random() < 0.6)
+        window = int(rng.integers(1, nk + 40)) if rng.random() < 0.35 else 0
+        wr = int(rng.integers(1, nk + 40)) if rng.random() < 0.2 else 0
+        sinks = int(rng.integers(1, 80)) if rng.random() < 0.2 else 0
+        padded = rng.random() < 0.5
+        lo = int(rng.integers(0, nk + 1)) if padded else 0
+        amp = float(rng.choice([0.5, 1.0, 1.0, 2.0]))
+        name = f"rand{len(cases):02d}"
+        cases.append(synth.Workload(
+            name, B=b, Hq=hkv * g, Hkv=hkv, Nq=nq, Nk=nk, d=d, dtype=dtype,
+            causal=causal, window=window, window_right=wr, sinks=sinks,
+            len_lo=lo if padded else 0, len_hi=nk if padded else 0,
+            amp=amp))
+    return cases
+
+
+CASES = _draw_cases()
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_random_shape(w):
+    gu.check_full(w.name, w, 1000 + int(w.name[4:]))
