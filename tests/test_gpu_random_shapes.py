@@ -55,3 +55,50 @@ CASES = _draw_cases()
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_random_shape(w):
     gu.check_full(w.name, w, 1000 + int(w.name[4:]))
+
+
+# ---- the backward pass on a seeded sweep -----------------------------------
+# Rows that see a single key have gradients that vanish only by cancellation
+# (their exact value is 0, the bf16 path leaves an fp32 residue), so the
+# sweep keeps every sequence at 8 keys or more and windows of 8 or more; a
+# tensor's bounds are stated against its own scale, as in the backward
+# tests.
+
+N_BWD_CASES = 48
+
+
+def _draw_bwd_cases(seed=20261205, n=N_BWD_CASES):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 3, 4, 7]))
+        nk = int(rng.integers(16, 600))
+        kind = rng.random()
+        nq = nk if kind < 0.6 else (1 if kind < 0.7 else
+                                   int(rng.integers(2, nk + 1)))
+        b = int(rng.integers(1, 4))
+        if b * hkv * g * nq * nk * d > 1.0e8:
+            continue
+        causal = bool(rng.random() < 0.6)
+        window = int(rng.integers(8, nk + 40)) if rng.random() < 0.3 else 0
+        wr = int(rng.integers(8, nk + 40)) if rng.random() < 0.2 else 0
+        sinks = int(rng.integers(1, 40)) if rng.random() < 0.2 else 0
+        padded = rng.random() < 0.5
+        lo = int(rng.integers(8, nk + 1)) if padded else 0
+        cases.append(synth.Workload(
+            f"bwdrand{len(cases):02d}", B=b, Hq=hkv * g, Hkv=hkv, Nq=nq,
+            Nk=nk, d=d, dtype="bf16", causal=causal, window=window,
+            window_right=wr, sinks=sinks, len_lo=lo if padded else 0,
+            len_hi=nk if padded else 0))
+    return cases
+
+
+BWD_CASES = _draw_bwd_cases()
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=lambda w: w.name)
+def test_random_shape_backward(w):
+    from tests.test_gpu_backward import check_bwd_full
+    check_bwd_full(w.name, w, 2000 + int(w.name[7:]))
