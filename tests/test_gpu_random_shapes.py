@@ -102,3 +102,53 @@ BWD_CASES = _draw_bwd_cases()
 def test_random_shape_backward(w):
     from tests.test_gpu_backward import check_bwd_full
     check_bwd_full(w.name, w, 2000 + int(w.name[7:]))
+
+
+# ---- the FP8 path on a seeded sweep ----------------------------------------
+# Each case: codes and scales bit for bit against the FP8 reference, then the
+# forward against the exact attention of the dequantized operands (the
+# checks and tolerances of the FP8 tests).
+
+N_FP8_CASES = 32
+
+
+def _draw_fp8_cases(seed=20261206, n=N_FP8_CASES):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 4, 7]))
+        nk = int(rng.integers(1, 700))
+        kind = rng.random()
+        nq = nk if kind < 0.6 else (1 if kind < 0.7 else
+                                   int(rng.integers(1, nk + 1)))
+        b = int(rng.integers(1, 4))
+        if b * hkv * g * nq * nk * d > 1.0e8:
+            continue
+        causal = bool(rng.random() < 0.6)
+        window = int(rng.integers(1, nk + 40)) if rng.random() < 0.3 else 0
+        wr = int(rng.integers(1, nk + 40)) if rng.random() < 0.2 else 0
+        sinks = int(rng.integers(1, 40)) if rng.random() < 0.2 else 0
+        padded = rng.random() < 0.5
+        lo = int(rng.integers(0, nk + 1)) if padded else 0
+        rot = bool(rng.random() < 0.7)
+        pt = bool(rng.random() < 0.2)
+        cases.append((synth.Workload(
+            f"fp8rand{len(cases):02d}", B=b, Hq=hkv * g, Hkv=hkv, Nq=nq,
+            Nk=nk, d=d, dtype="bf16", causal=causal, window=window,
+            window_right=wr, sinks=sinks, len_lo=lo if padded else 0,
+            len_hi=nk if padded else 0), rot, pt))
+    return cases
+
+
+FP8_CASES = _draw_fp8_cases()
+
+
+@pytest.mark.parametrize("w,rot,pt", FP8_CASES,
+                         ids=lambda c: getattr(c, "name", str(c)))
+def test_random_shape_fp8(w, rot, pt):
+    from tests.test_gpu_fp8 import (test_fp8_forward_matches_oracle,
+                                    test_fp8_quantize_bit_exact)
+    test_fp8_quantize_bit_exact(w, rot, pt)
+    test_fp8_forward_matches_oracle(w, rot, pt)
