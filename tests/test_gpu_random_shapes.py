@@ -152,3 +152,45 @@ def test_random_shape_fp8(w, rot, pt):
                                     test_fp8_quantize_bit_exact)
     test_fp8_quantize_bit_exact(w, rot, pt)
     test_fp8_forward_matches_oracle(w, rot, pt)
+
+
+# ---- medium sizes, sampled rows ---------------------------------------------
+# Launches of several rounds of the chip's workgroup slots (block orders with
+# and without bands, groups that do and do not divide over the XCDs, the
+# run-time causal tail), each checked on sampled rows (tile edges, the
+# valid-length boundary, random rows) computed by the oracle one by one.
+
+N_MEDIUM_CASES = 16
+
+
+def _draw_medium_cases(seed=20261207, n=N_MEDIUM_CASES):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 7]))
+        nk = int(rng.integers(1024, 8193))
+        nq = nk if rng.random() < 0.8 else int(rng.integers(2, nk + 1))
+        b = int(rng.integers(1, 5))
+        if b * hkv * g * nq * nk * d > 6e10:  # GPU time and memory
+            continue
+        causal = bool(rng.random() < 0.75)
+        window = int(rng.integers(64, nk)) if rng.random() < 0.25 else 0
+        sinks = int(rng.integers(1, 100)) if rng.random() < 0.15 else 0
+        padded = rng.random() < 0.4
+        lo = int(rng.integers(1, nk + 1)) if padded else 0
+        cases.append(synth.Workload(
+            f"medrand{len(cases):02d}", B=b, Hq=hkv * g, Hkv=hkv, Nq=nq,
+            Nk=nk, d=d, dtype="bf16", causal=causal or window > 0,
+            window=window, sinks=sinks, len_lo=lo if padded else 0,
+            len_hi=nk if padded else 0))
+    return cases
+
+
+MEDIUM_CASES = _draw_medium_cases()
+
+
+@pytest.mark.parametrize("w", MEDIUM_CASES, ids=lambda w: w.name)
+def test_random_medium_shape_sampled(w):
+    gu.check_sampled(w.name, w, 3000 + int(w.name[7:]))
