@@ -58,7 +58,9 @@
  * to finish: a call that grows the workspace synchronises the device.  Every
  * other call is asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream) and never synchronises; a caller that must not synchronise makes
- * one call of its largest size first.  The
+ * one call of its largest size first.  With the workspace at its size, a
+ * call is kernel launches on `stream` only, so it may be captured into a
+ * HIP graph and replayed.  The
  * library holds a lock from the size check through the launch, so calls
  * from several host threads never free a buffer a queued launch still
  * names; but all workspace users on one device share the one buffer, so
